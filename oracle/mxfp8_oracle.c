@@ -1,0 +1,364 @@
+/*
+ * mxfp8_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, single-threaded CPU definition of what the fused SwiGLU +
+ * MXFP8 cast computes.  It exists to check the HIP kernels: only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg load it.  It
+ * shares no code, header, table or constant with the GPU library and never
+ * includes anything from it.
+ *
+ * Sources (web pages, by title and section):
+ *  [P1] "Add swiglu + MXFP8 fused CuTe DSL kernel"
+ *       - Summary: one pass fuses swiglu with the RCEIL MXFP8 cast; gate/up
+ *         read once; rowwise (1x32), colwise (32x1) or both scale layouts.
+ *       - API: gated_input packs [gate | up]; backward takes grad_h and
+ *         returns [dGate | dUp].
+ *       - Numerics and tests: forward E4M3 data and E8M0 scales equal the
+ *         eager activation followed by the standalone quantizers, including
+ *         NaN/Inf, zero, subnormal-tiny and E4M3-boundary amax cases.
+ *       - commit message: a NaN/Inf amax invalidates the block (scale byte
+ *         255, all-NaN data); a byte-0 scale descales by 2^127.
+ *  [P3] "[mxfp8 moe training] update 3d quant colwise scaling kernel to use
+ *       single input/output TMA descriptors", Summary: the 3D (E,N,K)
+ *       colwise quant writes each expert column-major.
+ *  [P4] "[mxfp8 moe training] add compile support", Perf analysis: the 2D
+ *       colwise ("dim1") cast output is column-major.
+ *
+ * Readings where the pages are silent (each one is listed in the design
+ * notes of the repository):
+ *  - RCEIL: the scale is the smallest power of two 2^k, k in [-127, 127],
+ *    with amax <= 448 * 2^k, i.e. 2^ceil(log2(amax/448)) clamped to the E8M0
+ *    range; E8M0 byte = k + 127.  amax == 0 gives byte 0.
+ *  - E4M3 is OCP E4M3FN (bias 7, max 448, no infinities, 0x7F/0xFF NaN);
+ *    the element cast rounds to nearest, ties to even, and saturates to
+ *    +-448.  NaN data is written as 0x7F.
+ *  - Any NaN or +-Inf element invalidates its block.
+ *  - Eager forward rounds twice: s = bf16(silu(g)), h = bf16(s * u).
+ *  - Eager backward (autograd of silu(g) * u in bf16): du = bf16(dh * s),
+ *    ds = bf16(dh * u), dg = bf16(ds * sig * (1 + g * (1 - sig))).
+ *  - Scales are plain row-major: rowwise [M, W/32], colwise [W, M/32].
+ *    Colwise data is [W, M] row-major (the transpose of the [M, W] view).
+ *  - 3D: blocks of 32 along N; expert e's data at q[e][k][n], scales at
+ *    s[e][k][n/32].
+ *
+ * All real arithmetic here is IEEE double: a product of two bf16 values is
+ * exact in double, and silu/sigmoid carry ~1e-16 relative error before the
+ * single rounding to bf16.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_ROWWISE 1
+#define ORC_COLWISE 2
+
+/* ------------------------------------------------------------------ bf16 */
+
+/* bf16 is the top half of an IEEE binary32; widening is exact. */
+double orc_bf16_decode(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to bf16: 8 significant bits, round to nearest with ties
+ * to even, subnormal quantum 2^-133, overflow to +-Inf, NaN to 0x7FC0. */
+uint16_t orc_bf16_round(double v)
+{
+    if (isnan(v))
+        return 0x7FC0;
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    double a = fabs(v);
+    if (isinf(a))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);              /* a = f * 2^e with f in [0.5, 1)           */
+    int q = e - 8;             /* weight of the last kept bit (8 bits kept) */
+    if (q < -133)
+        q = -133;              /* below 2^-126 the spacing stays 2^-133     */
+    double r = ldexp(a, -q);   /* exact: a power-of-two scaling             */
+    double n = floor(r);
+    double frac = r - n;       /* exact                                     */
+    if (frac > 0.5 || (frac == 0.5 && fmod(n, 2.0) != 0.0))
+        n += 1.0;
+    double rounded = ldexp(n, q);
+    double bf16_max = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127             */
+    if (rounded > bf16_max)
+        return sign | 0x7F80;
+    float f = (float)rounded;  /* exact: 8 significant bits fit binary32   */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------ E4M3 */
+
+/* OCP E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent
+ * field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; no infinities. */
+double orc_e4m3_decode(uint8_t c)
+{
+    int s = c >> 7, e = (c >> 3) & 0xF, m = c & 0x7;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    double mag = (e == 0) ? ldexp((double)m, -9)            /* m/8 * 2^-6        */
+                          : ldexp((double)(8 + m), e - 10); /* (1+m/8) * 2^(e-7) */
+    return s ? -mag : mag;
+}
+
+/* Nearest E4M3 code to v: binary search over the 127 non-negative finite
+ * codes (their values increase with the code), ties to the even code,
+ * saturation to +-448 above the largest finite value, NaN -> 0x7F. */
+uint8_t orc_e4m3_encode(double v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int lo = 0, hi = 126;      /* decode(lo) <= a < decode(hi) */
+    while (hi - lo > 1) {
+        int mid = (lo + hi) / 2;
+        if (orc_e4m3_decode((uint8_t)mid) <= a)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    double below = a - orc_e4m3_decode((uint8_t)lo);
+    double above = orc_e4m3_decode((uint8_t)hi) - a;
+    int code;
+    if (below < above)
+        code = lo;
+    else if (above < below)
+        code = hi;
+    else
+        code = (lo % 2 == 0) ? lo : hi;
+    return sign | (uint8_t)code;
+}
+
+/* ------------------------------------------------------------------ E8M0 */
+
+/* RCEIL: the smallest k in [-127, 127] with amax <= 448 * 2^k; byte k+127.
+ * amax must be finite and >= 0. */
+uint8_t orc_e8m0_rceil(double amax)
+{
+    for (int k = -127; k <= 127; k++)
+        if (amax <= ldexp(448.0, k))
+            return (uint8_t)(k + 127);
+    return 254;
+}
+
+/* The real value an E8M0 byte stands for (255 is NaN). */
+double orc_e8m0_decode(uint8_t b)
+{
+    return b == 255 ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+/* ------------------------------------------------------- one 32-element block */
+
+/* Codes of n values at a given scale byte (x * 2^(127 - byte), then E4M3). */
+void orc_quant_block_at(const double *y, int64_t n, int64_t ystride,
+                        uint8_t scale, uint8_t *q, int64_t qstride)
+{
+    if (scale == 255) {
+        for (int64_t i = 0; i < n; i++)
+            q[i * qstride] = 0x7F;
+        return;
+    }
+    double descale = ldexp(1.0, 127 - (int)scale);
+    for (int64_t i = 0; i < n; i++)
+        q[i * qstride] = orc_e4m3_encode(y[i * ystride] * descale);
+}
+
+/* Scale byte of a block: 255 if any element is NaN or +-Inf, else RCEIL of
+ * the largest magnitude. */
+uint8_t orc_block_scale(const double *y, int64_t n, int64_t ystride)
+{
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; i++) {
+        double v = y[i * ystride];
+        if (!isfinite(v))
+            return 255;
+        if (fabs(v) > amax)
+            amax = fabs(v);
+    }
+    return orc_e8m0_rceil(amax);
+}
+
+void orc_quant_block(const double *y, int64_t n, int64_t ystride,
+                     uint8_t *q, int64_t qstride, uint8_t *s)
+{
+    *s = orc_block_scale(y, n, ystride);
+    orc_quant_block_at(y, n, ystride, *s, q, qstride);
+}
+
+/* -------------------------------------------------------------- activation */
+
+double orc_sigmoid(double x)
+{
+    if (isnan(x))
+        return x;
+    if (x >= 0.0)
+        return 1.0 / (1.0 + exp(-x));
+    double t = exp(x);         /* no overflow for very negative x */
+    return t / (1.0 + t);
+}
+
+double orc_silu(double x)
+{
+    return x * orc_sigmoid(x); /* -Inf * 0 = NaN, +Inf * 1 = +Inf */
+}
+
+/* Forward value of one element as eager bf16 computes it: two roundings. */
+static uint16_t fwd_value(uint16_t g, uint16_t u)
+{
+    uint16_t s = orc_bf16_round(orc_silu(orc_bf16_decode(g)));
+    return orc_bf16_round(orc_bf16_decode(s) * orc_bf16_decode(u));
+}
+
+/* Backward values of one element (eager autograd of silu(g) * u). */
+static void bwd_value(uint16_t dh, uint16_t g, uint16_t u, uint16_t *dg, uint16_t *du)
+{
+    double gv = orc_bf16_decode(g), uv = orc_bf16_decode(u), dhv = orc_bf16_decode(dh);
+    double sig = orc_sigmoid(gv);
+    uint16_t s = orc_bf16_round(gv * sig);
+    *du = orc_bf16_round(dhv * orc_bf16_decode(s));
+    uint16_t ds = orc_bf16_round(dhv * uv);
+    *dg = orc_bf16_round(orc_bf16_decode(ds) * sig * (1.0 + gv * (1.0 - sig)));
+}
+
+void orc_swiglu_fwd_values(const uint16_t *g, const uint16_t *u, int64_t n, uint16_t *h)
+{
+    for (int64_t i = 0; i < n; i++)
+        h[i] = fwd_value(g[i], u[i]);
+}
+
+void orc_swiglu_bwd_values(const uint16_t *dh, const uint16_t *g, const uint16_t *u,
+                           int64_t n, uint16_t *dg, uint16_t *du)
+{
+    for (int64_t i = 0; i < n; i++)
+        bwd_value(dh[i], g[i], u[i], &dg[i], &du[i]);
+}
+
+/* ------------------------------------------------------------ matrix level */
+
+typedef struct {
+    uint8_t *q_row; int64_t ld_q_row; uint8_t *s_row; int64_t ld_s_row;
+    uint8_t *q_col; int64_t ld_q_col; uint8_t *s_col; int64_t ld_s_col;
+} orc_out;
+
+/* Quantize a slab of R <= 32 rows (starting at row m0) of a [*, W] matrix
+ * y held as doubles, row stride W.  Colwise needs a full 32-row slab. */
+static void quant_slab(const double *y, int64_t R, int64_t W, int64_t m0,
+                       int layout, const orc_out *o)
+{
+    if (layout & ORC_ROWWISE)
+        for (int64_t r = 0; r < R; r++)
+            for (int64_t c0 = 0; c0 < W; c0 += 32)
+                orc_quant_block(y + r * W + c0, 32, 1,
+                                o->q_row + (m0 + r) * o->ld_q_row + c0, 1,
+                                o->s_row + (m0 + r) * o->ld_s_row + c0 / 32);
+    if (layout & ORC_COLWISE)
+        for (int64_t c = 0; c < W; c++)
+            orc_quant_block(y + c, 32, W,
+                            o->q_col + c * o->ld_q_col + m0, 1,
+                            o->s_col + c * o->ld_s_col + m0 / 32);
+}
+
+enum { OP_QUANT = 0, OP_FWD = 1, OP_BWD = 2 };
+
+/* Shared driver: builds the [M, W] values slab by slab, then quantizes. */
+static int run(int op, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+               const uint16_t *c, int64_t ldc, int64_t M, int64_t N, int layout,
+               const orc_out *o)
+{
+    if (M < 0 || N < 0 || layout < 1 || layout > 3)
+        return -1;
+    if ((layout & ORC_COLWISE) && M % 32 != 0)
+        return -1;
+    if (op != OP_QUANT && N % 32 != 0)
+        return -1;
+    if (op == OP_QUANT && (layout & ORC_ROWWISE) && N % 32 != 0)
+        return -1;
+    int64_t W = (op == OP_BWD) ? 2 * N : N;
+    double *y = (double *)malloc(sizeof(double) * 32 * (size_t)(W > 0 ? W : 1));
+    if (!y)
+        return -2;
+    for (int64_t m0 = 0; m0 < M; m0 += 32) {
+        int64_t R = (M - m0 < 32) ? M - m0 : 32;
+        for (int64_t r = 0; r < R; r++) {
+            int64_t m = m0 + r;
+            double *yr = y + r * W;
+            for (int64_t j = 0; j < N; j++) {
+                if (op == OP_QUANT) {
+                    yr[j] = orc_bf16_decode(a[m * lda + j]);
+                } else if (op == OP_FWD) {
+                    yr[j] = orc_bf16_decode(fwd_value(a[m * lda + j], b[m * ldb + j]));
+                } else {
+                    uint16_t dg, du;
+                    bwd_value(a[m * lda + j], b[m * ldb + j], c[m * ldc + j], &dg, &du);
+                    yr[j] = orc_bf16_decode(dg);
+                    yr[N + j] = orc_bf16_decode(du);
+                }
+            }
+        }
+        quant_slab(y, R, W, m0, layout, o);
+    }
+    free(y);
+    return 0;
+}
+
+int orc_quant_2d(const uint16_t *x, int64_t ld_x, int64_t M, int64_t K, int layout,
+                 uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
+                 uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
+{
+    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
+    return run(OP_QUANT, x, ld_x, NULL, 0, NULL, 0, M, K, layout, &o);
+}
+
+int orc_swiglu_fwd(const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
+                   int64_t M, int64_t N, int layout,
+                   uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
+                   uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
+{
+    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
+    return run(OP_FWD, gate, ld_gate, up, ld_up, NULL, 0, M, N, layout, &o);
+}
+
+int orc_swiglu_bwd(const uint16_t *dh, int64_t ld_dh, const uint16_t *gate, int64_t ld_gate,
+                   const uint16_t *up, int64_t ld_up, int64_t M, int64_t N, int layout,
+                   uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
+                   uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
+{
+    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
+    return run(OP_BWD, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout, &o);
+}
+
+/* 3D per-expert colwise quant [P3, Summary]: expert e is the [N, K] matrix
+ * w + e*stride_e (row stride ld_w); its 32x1 blocks run along N.  Output q
+ * is column-major per expert, q[e*N*K + k*N + n]; scales s[e*K*(N/32) +
+ * k*(N/32) + n/32]. */
+int orc_quant_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K,
+                         int64_t stride_e, int64_t ld_w, uint8_t *q, uint8_t *s)
+{
+    if (E < 0 || N < 0 || K < 0 || N % 32 != 0)
+        return -1;
+    double *blk = (double *)malloc(sizeof(double) * 32);
+    if (!blk)
+        return -2;
+    for (int64_t e = 0; e < E; e++)
+        for (int64_t k = 0; k < K; k++)
+            for (int64_t n0 = 0; n0 < N; n0 += 32) {
+                for (int64_t i = 0; i < 32; i++)
+                    blk[i] = orc_bf16_decode(w[e * stride_e + (n0 + i) * ld_w + k]);
+                orc_quant_block(blk, 32, 1, q + e * N * K + k * N + n0, 1,
+                                s + e * K * (N / 32) + k * (N / 32) + n0 / 32);
+            }
+    free(blk);
+    return 0;
+}
