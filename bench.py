@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused SwiGLU + MXFP8 cast on one MI355X.
+
+A step is one pass of the hot path over one batch: the fused forward and
+the fused backward, each emitting both scale layouts (rowwise 1x32 and
+colwise 32x1) in one launch, on 131072 x 8192 activations (gate/up the two
+halves of a 131072 x 16384 bf16 w13 tensor, dh 131072 x 8192; N(0, 1)
+synthetic values).  Throughput is achieved HBM bandwidth: algorithmic bytes
+(inputs read once, E4M3 data and E8M0 scales written once per layout) over
+time, the accounting the pages' tables use ("Add swiglu + MXFP8 fused CuTe
+DSL kernel", Performance).  Inputs are resident in HBM before timing.
+
+Prints ONE JSON line.  Extra fields: `roofline` (dominant kernel, HIP-event
+timing on the launch stream), `cpu_baseline` (the CPU oracle on a bounded
+sample of the same workload), `detail` (each op and layout alone, the 3D
+expert cast, a copy-kernel ceiling).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused SwiGLU+MXFP8 cast achieved HBM GB/s (% of peak), fwd/bwd, both scales"
+M_ROWS, N_COLS = 131072, 8192
+WORKLOAD = "swiglu_131072x8192_w13"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_bwd_both_131072x8192.json")
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle processes")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--no-detail", action="store_true", help="skip the per-op breakdown")
+    p.add_argument("--validate", action="store_true", help="check sampled outputs against the oracle before timing")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "swiglu_activation_cast_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def time_launches(fn, iters, warmup):
+    """Average duration (s) of fn's launch, HIP events on torch's current
+    stream (the stream the binding launches on)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return sum(ms) / len(ms) / 1e3, ms[len(ms) // 2] / 1e3
+
+
+def cpu_baseline(inp, rows: int):
+    """The oracle as it stands, single-threaded, on the first `rows` rows of
+    the workload: fused forward and backward, both layouts."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from swiglu_activation_cast_amd import metrics
+
+    def bits(t):
+        return t[:rows].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    g, u, dh = bits(inp.gate), bits(inp.up), bits(inp.dh)
+    t0 = time.perf_counter()
+    oracle.swiglu_fwd(g, u, oracle.BOTH)
+    oracle.swiglu_bwd(dh, g, u, oracle.BOTH)
+    dt = time.perf_counter() - t0
+    nbytes = metrics.swiglu_fwd_bytes(rows, N_COLS, 3) + metrics.swiglu_bwd_bytes(rows, N_COLS, 3)
+    return {
+        "value": round(metrics.gbps(nbytes, dt), 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"first {rows} rows of the {M_ROWS}x{N_COLS} workload, fused fwd + bwd, both layouts "
+                  f"({dt:.1f} s of single-threaded C)",
+        "seconds": round(dt, 3),
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def validate(inp):
+    """Sampled slabs of the forward and backward against the oracle (codes
+    within one step, scales equal except at a power-of-two boundary)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import swiglu_activation_cast_amd as mx
+
+    def bits(t):
+        return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+    def ordinal(c):
+        c = c.astype(np.int32)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+
+    fwd = mx.mxfp8_swiglu_fwd(inp.gate, inp.up, rowwise=True, colwise=True)
+    bwd = mx.mxfp8_swiglu_bwd(inp.dh, inp.gate, inp.up, rowwise=True, colwise=True)
+    torch.cuda.synchronize()
+    for sb in (0, 1777, M_ROWS // 32 - 1):
+        r0, r1 = sb * 32, sb * 32 + 32
+        g, u, dh = bits(inp.gate[r0:r1]), bits(inp.up[r0:r1]), bits(inp.dh[r0:r1])
+        for name, outs, orc in (("fwd", fwd, oracle.swiglu_fwd(g, u, 3)), ("bwd", bwd, oracle.swiglu_bwd(dh, g, u, 3))):
+            q_row, q_col, s_row, s_col = outs
+            pairs = ((q_row[r0:r1], s_row[r0:r1], orc[0], orc[1]),
+                     (q_col[:, r0:r1], s_col[:, sb:sb + 1], orc[2], orc[3]))
+            for q, s, oq, os_ in pairs:
+                q, s = q.cpu().numpy(), s.cpu().numpy()
+                same = s == os_
+                if (~same).sum() > 1:
+                    raise SystemExit(f"validation failed: {name} slab {sb}: {(~same).sum()} scales differ")
+                qb = q.reshape(s.shape[0], s.shape[1], 32)[same]
+                ob = oq.reshape(s.shape[0], s.shape[1], 32)[same]
+                if np.abs(ordinal(qb) - ordinal(ob)).max(initial=0) > 1:
+                    raise SystemExit(f"validation failed: {name} slab {sb}: codes differ by more than one step")
+    del fwd, bwd
+    torch.cuda.empty_cache()
+    print("validate: sampled slabs match the oracle", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the cast shards rows or experts "
+              "across GPUs with no exchange, so the one-GPU number is the per-GPU figure.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import swiglu_activation_cast_amd as mx
+    from swiglu_activation_cast_amd import metrics, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"bench: generating {WORKLOAD} on {torch.cuda.get_device_name(dev)}", file=sys.stderr, flush=True)
+    inp = synth.workload(WORKLOAD, device=dev)
+    if args.validate:
+        validate(inp)
+
+    M, N = M_ROWS, N_COLS
+    fwd_out = mx.alloc_outputs(M, N, mx.BOTH, dev)
+    bwd_out = mx.alloc_outputs(M, 2 * N, mx.BOTH, dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        mx.mxfp8_swiglu_fwd(inp.gate, inp.up, rowwise=True, colwise=True, out=fwd_out, stream=stream)
+
+    def bwd():
+        mx.mxfp8_swiglu_bwd(inp.dh, inp.gate, inp.up, rowwise=True, colwise=True, out=bwd_out, stream=stream)
+
+    fwd_bytes = metrics.swiglu_fwd_bytes(M, N, mx.BOTH)
+    bwd_bytes = metrics.swiglu_bwd_bytes(M, N, mx.BOTH)
+    step_bytes = fwd_bytes + bwd_bytes
+
+    # ---- the step: warmup, then exactly K timed steps between synchronizations
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    ev_f = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev_b = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev_f[i][0].record(stream)
+        fwd()
+        ev_f[i][1].record(stream)
+        ev_b[i][0].record(stream)
+        bwd()
+        ev_b[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"bench: {args.steps} steps done", file=sys.stderr, flush=True)
+    fwd_s = sum(a.elapsed_time(b) for a, b in ev_f) / args.steps / 1e3
+    bwd_s = sum(a.elapsed_time(b) for a, b in ev_b) / args.steps / 1e3
+    step_s = wall / args.steps
+    value = metrics.gbps(step_bytes, step_s)
+
+    # ---- roofline of the dominant kernel (the backward, both layouts)
+    dom_bytes, dom_s, dom_name = (bwd_bytes, bwd_s, "k_tiled<OpBwd, rowwise+colwise>")
+    if fwd_s > bwd_s:
+        dom_bytes, dom_s, dom_name = (fwd_bytes, fwd_s, "k_tiled<OpFwd, rowwise+colwise>")
+    achieved = metrics.gbps(dom_bytes, dom_s)
+    traffic = None
+    src_hash = kernel_source_hash()
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == src_hash:
+            traffic = tr.get("hbm_bytes_per_launch")
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": metrics.HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(achieved / metrics.HBM_PEAK_GBPS, 4),
+        "traffic": traffic,
+        "kernel": dom_name,
+        "algorithmic_bytes": dom_bytes,
+        "avg_launch_us": round(dom_s * 1e6, 2),
+    }
+
+    detail = {}
+    if not args.no_detail:
+        detail = run_detail(inp, fwd_out, bwd_out, stream)
+
+    cpu = None
+    if not args.no_cpu:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, args.cpu_rows)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "fused SwiGLU fwd + bwd, rowwise+colwise MXFP8 in one pass each, M=131072, N=8192, "
+                        "gate/up halves of a bf16 w13 [131072, 16384], dh [131072, 8192], N(0,1)",
+            "M": M,
+            "N": N,
+            "layout": "both",
+            "step_bytes": step_bytes,
+            "fraction_of_peak": round(value / metrics.HBM_PEAK_GBPS, 4),
+            "fwd_us": round(fwd_s * 1e6, 2),
+            "bwd_us": round(bwd_s * 1e6, 2),
+            "kernel_source_hash": src_hash,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_detail(inp, fwd_out, bwd_out, stream):
+    """Each op and layout alone at the same size, the 3D expert cast, and a
+    device copy of the w13 tensor as a bandwidth ceiling."""
+    import torch
+
+    import swiglu_activation_cast_amd as mx
+    from swiglu_activation_cast_amd import metrics, synth
+
+    M, N = M_ROWS, N_COLS
+    res = {}
+    for lay, name in ((mx.ROWWISE, "row"), (mx.COLWISE, "col"), (mx.BOTH, "both")):
+        fl = dict(rowwise=bool(lay & 1), colwise=bool(lay & 2))
+        f = lambda: mx.mxfp8_swiglu_fwd(inp.gate, inp.up, out=fwd_out, stream=stream, **fl)
+        b = lambda: mx.mxfp8_swiglu_bwd(inp.dh, inp.gate, inp.up, out=bwd_out, stream=stream, **fl)
+        for op, fn, nbytes in (("fwd", f, metrics.swiglu_fwd_bytes(M, N, lay)),
+                               ("bwd", b, metrics.swiglu_bwd_bytes(M, N, lay))):
+            avg, med = time_launches(fn, 10, 2)
+            res[f"{op}_{name}"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nbytes, avg), 1),
+                                   "frac": round(metrics.gbps(nbytes, avg) / metrics.HBM_PEAK_GBPS, 4)}
+    print("bench: per-layout timing done", file=sys.stderr, flush=True)
+    # plain 2D cast of the gate half (colwise, the "dim1" cast) and rowwise
+    for lay, name in ((mx.ROWWISE, "row"), (mx.COLWISE, "col")):
+        fl = dict(rowwise=bool(lay & 1), colwise=bool(lay & 2))
+        fn = lambda: mx.mxfp8_quant_2d(inp.dh, out=fwd_out, stream=stream, **fl)
+        avg, _ = time_launches(fn, 10, 2)
+        nb = metrics.quant_2d_bytes(M, N, lay)
+        res[f"quant2d_{name}"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nb, avg), 1),
+                                  "frac": round(metrics.gbps(nb, avg) / metrics.HBM_PEAK_GBPS, 4)}
+    # copy ceiling: device-to-device copy of the 4 GiB w13 tensor
+    dst = torch.empty_like(inp.w13)
+    avg, _ = time_launches(lambda: dst.copy_(inp.w13), 10, 2)
+    res["copy_ceiling"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(2 * inp.w13.numel() * 2, avg), 1)}
+    del dst
+    torch.cuda.empty_cache()
+    # 3D expert cast, 64 experts of 8192 x 5120 (inputs 5.4 GB)
+    w = synth.expert_workload(64, device=inp.gate.device)
+    q = torch.empty((64, 5120, 8192), dtype=torch.uint8, device=w.device)
+    s = torch.empty((64, 5120, 256), dtype=torch.uint8, device=w.device)
+    avg, _ = time_launches(lambda: mx.mxfp8_quant_3d_colwise(w, out=(q, s), stream=stream), 10, 2)
+    nb = metrics.quant_3d_bytes(64, 8192, 5120)
+    res["quant3d_E64"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nb, avg), 1),
+                          "frac": round(metrics.gbps(nb, avg) / metrics.HBM_PEAK_GBPS, 4)}
+    del w, q, s
+    torch.cuda.empty_cache()
+    print("bench: detail done", file=sys.stderr, flush=True)
+    return res
+
+
+if __name__ == "__main__":
+    main()

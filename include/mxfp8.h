@@ -1,0 +1,135 @@
+/*
+ * mxfp8.h -- C ABI of the MI355X (gfx950) fused SwiGLU + MXFP8 cast library
+ * (libmxfp8.so).
+ *
+ * MXFP8 here: blocks of 32 consecutive elements (along a row for the rowwise
+ * 1x32 layout, along a column for the colwise 32x1 layout) share one E8M0
+ * scale byte b, standing for 2^(b-127).  b is chosen by RCEIL: the smallest
+ * power of two 2^k (k in [-127, 127]) with amax <= 448 * 2^k, where amax is
+ * the block's largest magnitude.  Each element x is stored as the FP8 E4M3
+ * (OCP E4M3FN) code of x * 2^(127-b), rounded to nearest with ties to even
+ * and saturated to +-448.  A block holding any NaN or +-Inf gets scale byte
+ * 255 and data 0x7F in all 32 places; an all-zero block gets byte 0.
+ * Source: "Add swiglu + MXFP8 fused CuTe DSL kernel" (Summary; Numerics and
+ * tests; commit message).
+ *
+ * Conventions shared by every call:
+ *  - All data pointers are DEVICE pointers.  bf16 inputs are raw 16-bit
+ *    patterns; outputs are bytes (E4M3 codes, E8M0 scales).
+ *  - Dimensions and leading dimensions (ld_*) are int64 element counts
+ *    (bytes for the 1-byte outputs).  Every matrix is row-major with unit
+ *    column stride and the given row stride.
+ *  - layout is MXFP8_ROWWISE, MXFP8_COLWISE or MXFP8_BOTH.  Rowwise outputs
+ *    are q_row [M, W] and s_row [M, W/32]; colwise outputs are q_col [W, M]
+ *    (the column-major form of the [M, W] result, one output row per input
+ *    column) and s_col [W, M/32].  Pointers of a layout that is not asked
+ *    for are ignored and may be NULL.
+ *  - The caller owns and allocates every buffer.  The library never
+ *    allocates, frees, synchronizes or reads device memory from the host.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream).  The call returns once the kernel is enqueued.
+ *  - Every argument is checked before any HIP call; a failed check returns a
+ *    status and enqueues nothing.  M == 0 or a zero width returns MXFP8_OK
+ *    and enqueues nothing.
+ *  - Alignment: input pointers and E4M3 output pointers 16-byte aligned,
+ *    bf16 ld_* multiples of 8 elements, E4M3 ld_* multiples of 16 bytes.
+ *    Scale pointers and scale ld_* have no alignment requirement.
+ *  - Outputs must not alias inputs or each other (not checked).
+ *  - Calls are thread-safe; the library keeps no mutable global state.
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mxfp8_status {
+    MXFP8_OK = 0,
+    MXFP8_ERR_NULL = 1,     /* a pointer the layout needs is NULL                 */
+    MXFP8_ERR_SHAPE = 2,    /* negative dim, or a blocked dim not a multiple of 32 */
+    MXFP8_ERR_STRIDE = 3,   /* ld smaller than the row, or not a vector multiple   */
+    MXFP8_ERR_ALIGN = 4,    /* input or E4M3 output pointer not 16-byte aligned    */
+    MXFP8_ERR_LAYOUT = 5,   /* layout flags not in {1, 2, 3}                       */
+    MXFP8_ERR_OVERFLOW = 6, /* an extent overflows int64, or the grid is too large */
+    MXFP8_ERR_LAUNCH = 7    /* the HIP runtime refused the launch                  */
+} mxfp8_status;
+
+enum { MXFP8_ROWWISE = 1, MXFP8_COLWISE = 2, MXFP8_BOTH = 3 };
+
+/*
+ * Fused forward: h = silu(gate) * up, cast to MXFP8; h is never written.
+ * "Add swiglu + MXFP8 fused CuTe DSL kernel", Summary and API: gate and up
+ * are the two halves of the [M, 2N] fused w13 projection ([gate | up]), read
+ * once.  Pass gate = w13, up = w13 + N, ld_gate = ld_up = 2N for that
+ * layout, or two separate [M, N] tensors.
+ *   gate, up : bf16 [M, N], row strides ld_gate, ld_up.
+ *   W = N.  Requires N % 32 == 0; colwise also M % 32 == 0.
+ * Values: h = bf16(bf16(silu(g)) * u) computed in fp32 (two bf16
+ * roundings, as eager bf16 does); codes may differ from an exact evaluation
+ * by one E4M3 step where fp32 rounding moves h across a bf16 boundary.
+ */
+mxfp8_status mxfp8_swiglu_fwd(const void *gate, int64_t ld_gate,
+                              const void *up, int64_t ld_up,
+                              int64_t M, int64_t N, int layout,
+                              void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                              void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                              void *stream);
+
+/*
+ * Fused backward of h = silu(gate) * up for upstream gradient dh.
+ * "Add swiglu + MXFP8 fused CuTe DSL kernel", API: returns [dGate | dUp]
+ * concatenated along the width, so W = 2N: rowwise q_row [M, 2N] holds dGate
+ * in columns [0, N) and dUp in [N, 2N); colwise q_col [2N, M] holds dGate in
+ * rows [0, N) and dUp in rows [N, 2N).
+ *   dh, gate, up : bf16 [M, N], row strides ld_dh, ld_gate, ld_up.
+ *   Requires N % 32 == 0; colwise also M % 32 == 0.
+ * Values (eager bf16 autograd): s = bf16(silu(g)), du = bf16(dh * s),
+ * ds = bf16(dh * up), dg = bf16(ds * sig(g) * (1 + g * (1 - sig(g)))).
+ */
+mxfp8_status mxfp8_swiglu_bwd(const void *dh, int64_t ld_dh,
+                              const void *gate, int64_t ld_gate,
+                              const void *up, int64_t ld_up,
+                              int64_t M, int64_t N, int layout,
+                              void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                              void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                              void *stream);
+
+/*
+ * Plain MXFP8 cast of a bf16 matrix x [M, K] (row stride ld_x): the
+ * standalone quantizer the fused kernels are bit-compatible with ("Add
+ * swiglu + MXFP8 fused CuTe DSL kernel", Summary), and the 2D colwise
+ * ("dim1") cast ("[mxfp8 moe training] add compile support", Perf analysis).
+ *   W = K.  Rowwise requires K % 32 == 0; colwise requires M % 32 == 0 and
+ *   K % 8 == 0.  Results are exact (bit-identical to the definition).
+ */
+mxfp8_status mxfp8_quant_2d(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout,
+                            void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                            void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                            void *stream);
+
+/*
+ * 3D per-expert colwise cast of expert weights w (E, N, K), bf16: expert e
+ * is the [N, K] matrix at w + e * stride_e with row stride ld_w (packed:
+ * stride_e = N * K, ld_w = K).  Blocks of 32 run along N.  Output is
+ * column-major per expert: q (E, K, N) packed, element (e, n, k) at
+ * q[e*K*N + k*N + n]; scales s (E, K, N/32) packed, at s[e*K*(N/32) +
+ * k*(N/32) + n/32].  One launch covers all experts.
+ * "[mxfp8 moe training] update 3d quant colwise scaling kernel to use single
+ * input/output TMA descriptors", Summary.
+ *   Requires N % 32 == 0, K % 8 == 0, stride_e >= N * ld_w.  Exact results.
+ */
+mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t K,
+                                    int64_t stride_e, int64_t ld_w,
+                                    void *q, void *s, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *mxfp8_status_str(mxfp8_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP8_H */

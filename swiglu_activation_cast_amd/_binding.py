@@ -1,0 +1,215 @@
+"""ctypes binding of libmxfp8.so (argument marshalling only).
+
+Every function here takes torch tensors that live on the GPU, checks
+dtypes and devices, allocates the outputs with torch when the caller does
+not pass them, and calls the C entry point of the same name on torch's
+current stream.  All computation happens in the HIP kernels; there is no
+CPU or PyTorch fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Output tuple order follows the pages' API ("Add swiglu + MXFP8 fused CuTe
+DSL kernel", API): (output_rowwise, output_colwise, scales_rowwise,
+scales_colwise); a layout that was not asked for comes back as an empty
+tensor.  E4M3 data and E8M0 scales are returned as uint8 tensors (use
+``.view(torch.float8_e4m3fn)`` / ``.view(torch.float8_e8m0fnu)`` to
+reinterpret).  The colwise data is the [W, M] row-major tensor, i.e. the
+column-major storage of the [M, W] result (``q_col.t()`` is that view).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+ROWWISE = 1
+COLWISE = 2
+BOTH = 3
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmxfp8.so")
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_int = ctypes.c_int
+
+_SIGNATURES = {
+    "mxfp8_swiglu_fwd": [_p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
+    "mxfp8_swiglu_bwd": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
+    "mxfp8_quant_2d": [_p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
+    "mxfp8_quant_3d_colwise": [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p],
+}
+
+_lib = None
+
+
+class Mxfp8Error(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libmxfp8.so with argument types set (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m swiglu_activation_cast_amd._build` "
+            "(or __graft_entry__.build()) first"
+        )
+    handle = ctypes.CDLL(LIB_PATH)
+    for name, argtypes in _SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.argtypes = argtypes
+        fn.restype = _int
+    handle.mxfp8_status_str.argtypes = [_int]
+    handle.mxfp8_status_str.restype = ctypes.c_char_p
+    _lib = handle
+    return handle
+
+
+def status_str(status: int) -> str:
+    return lib().mxfp8_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise Mxfp8Error(fn, status, status_str(status))
+
+
+def _stream(device: torch.device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _bf16_matrix(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.data_ptr(), t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def _layout(rowwise: bool, colwise: bool) -> int:
+    layout = (ROWWISE if rowwise else 0) | (COLWISE if colwise else 0)
+    if layout == 0:
+        raise ValueError("at least one of rowwise / colwise must be set")
+    return layout
+
+
+def alloc_outputs(M: int, W: int, layout: int, device) -> Tuple[torch.Tensor, ...]:
+    """Empty (q_row, q_col, s_row, s_col) for an [M, W] result."""
+    empty = torch.empty(0, dtype=torch.uint8, device=device)
+    q_row = torch.empty((M, W), dtype=torch.uint8, device=device) if layout & ROWWISE else empty
+    s_row = torch.empty((M, W // 32), dtype=torch.uint8, device=device) if layout & ROWWISE else empty
+    q_col = torch.empty((W, M), dtype=torch.uint8, device=device) if layout & COLWISE else empty
+    s_col = torch.empty((W, M // 32), dtype=torch.uint8, device=device) if layout & COLWISE else empty
+    return q_row, q_col, s_row, s_col
+
+
+def _out_args(outs: Sequence[torch.Tensor], layout: int):
+    q_row, q_col, s_row, s_col = outs
+
+    def mat(t, on):
+        if not on:
+            return [None, 0]
+        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError("outputs must be 2-D uint8 GPU tensors with unit column stride")
+        return [t.data_ptr(), t.stride(0)]
+
+    return mat(q_row, layout & ROWWISE) + mat(s_row, layout & ROWWISE) + mat(q_col, layout & COLWISE) + mat(
+        s_col, layout & COLWISE
+    )
+
+
+def mxfp8_swiglu_fwd(gate: torch.Tensor, up: torch.Tensor, *, rowwise: bool = True, colwise: bool = False,
+                     out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """MXFP8 cast of silu(gate) * up; returns (q_row, q_col, s_row, s_col)."""
+    layout = _layout(rowwise, colwise)
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if gate.shape != up.shape or gate.device != up.device:
+        raise ValueError("gate and up must have the same shape and device")
+    M, N = gate.shape
+    outs = out if out is not None else alloc_outputs(M, N, layout, gate.device)
+    st = lib().mxfp8_swiglu_fwd(pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+                                _stream(gate.device, stream))
+    _check("mxfp8_swiglu_fwd", st)
+    return tuple(outs)
+
+
+def mxfp8_swiglu_bwd(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, *, rowwise: bool = True,
+                     colwise: bool = False, out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """MXFP8 cast of [dgate | dup]; returns (q_row, q_col, s_row, s_col) of width 2N."""
+    layout = _layout(rowwise, colwise)
+    pd, ldd = _bf16_matrix(dh, "dh")
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if not (dh.shape == gate.shape == up.shape) or not (dh.device == gate.device == up.device):
+        raise ValueError("dh, gate and up must have the same shape and device")
+    M, N = gate.shape
+    outs = out if out is not None else alloc_outputs(M, 2 * N, layout, gate.device)
+    st = lib().mxfp8_swiglu_bwd(pd, ldd, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+                                _stream(gate.device, stream))
+    _check("mxfp8_swiglu_bwd", st)
+    return tuple(outs)
+
+
+def mxfp8_quant_2d(x: torch.Tensor, *, rowwise: bool = True, colwise: bool = False,
+                   out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """Plain MXFP8 cast of a bf16 [M, K] matrix; returns (q_row, q_col, s_row, s_col)."""
+    layout = _layout(rowwise, colwise)
+    px, ldx = _bf16_matrix(x, "x")
+    M, K = x.shape
+    outs = out if out is not None else alloc_outputs(M, K, layout, x.device)
+    st = lib().mxfp8_quant_2d(px, ldx, M, K, layout, *_out_args(outs, layout), _stream(x.device, stream))
+    _check("mxfp8_quant_2d", st)
+    return tuple(outs)
+
+
+def mxfp8_quant_3d_colwise(w: torch.Tensor, *, out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """3D per-expert colwise cast of bf16 w (E, N, K); returns (q (E, K, N), s (E, K, N/32))."""
+    if w.dtype != torch.bfloat16 or not w.is_cuda or w.dim() != 3:
+        raise ValueError("w must be a 3-D bfloat16 GPU tensor")
+    E, N, K = w.shape
+    if K > 1 and w.stride(2) != 1:
+        raise ValueError("w must have unit stride along K")
+    if out is None:
+        q = torch.empty((E, K, N), dtype=torch.uint8, device=w.device)
+        s = torch.empty((E, K, N // 32), dtype=torch.uint8, device=w.device)
+    else:
+        q, s = out
+        if not (q.is_contiguous() and s.is_contiguous() and q.dtype == s.dtype == torch.uint8):
+            raise ValueError("3D outputs must be contiguous uint8 tensors")
+        if q.numel() != E * K * N or s.numel() != E * K * (N // 32):
+            raise ValueError("3D output sizes do not match (E, K, N) and (E, K, N/32)")
+    ld_w = w.stride(1) if N > 1 else K
+    stride_e = w.stride(0) if E > 1 else N * ld_w
+    st = lib().mxfp8_quant_3d_colwise(w.data_ptr(), E, N, K, stride_e, ld_w, q.data_ptr(), s.data_ptr(),
+                                      _stream(w.device, stream))
+    _check("mxfp8_quant_3d_colwise", st)
+    return q, s
+
+
+def gated_act_mxfp8_forward(gated_input: torch.Tensor, *, rowwise: bool = True, colwise: bool = False, out=None,
+                            stream=None):
+    """Forward on the packed [M, 2N] = [gate | up] projection (the pages' API name)."""
+    N = gated_input.shape[1] // 2
+    return mxfp8_swiglu_fwd(gated_input[:, :N], gated_input[:, N:], rowwise=rowwise, colwise=colwise, out=out,
+                            stream=stream)
+
+
+def gated_act_mxfp8_backward(grad_h: torch.Tensor, gated_input: torch.Tensor, *, rowwise: bool = True,
+                             colwise: bool = False, out=None, stream=None):
+    """Backward on the packed [M, 2N] = [gate | up] projection; outputs [dgate | dup]."""
+    N = gated_input.shape[1] // 2
+    return mxfp8_swiglu_bwd(grad_h, gated_input[:, :N], gated_input[:, N:], rowwise=rowwise, colwise=colwise,
+                            out=out, stream=stream)

@@ -1,0 +1,230 @@
+// mxfp8.hip -- C ABI of libmxfp8.so: argument checks and kernel launches.
+//
+// Every entry point validates its arguments on the host before touching
+// the HIP runtime, picks one kernel instantiation, sizes its grid and
+// enqueues it on the caller's stream.  Nothing is allocated, synchronized
+// or read back.  API shape: "Add swiglu + MXFP8 fused CuTe DSL kernel",
+// API (forward/backward with rowwise/colwise switches, fixed-arity
+// outputs) and Numerics and tests (launcher guards on sizes and pointer
+// alignment, each error path reachable without a device).
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdint.h>
+
+#include "mx_kernels.hpp"
+#include "mxfp8.h"
+
+namespace {
+
+using mx::Args;
+
+constexpr int kRowUnroll = 4;
+
+enum class Kind { Quant, Fwd, Bwd };
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+bool add_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_add_overflow(a, b, r); }
+
+// Largest offset touched in a [rows, cols] matrix with row stride ld, plus
+// one, must fit int64 (with room for a batch offset added on top).
+bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
+  if (rows == 0 || cols == 0) return true;
+  int64_t r;
+  return mul_ok(rows - 1, ld, &r) && add_ok(r, cols, &r) && r < (INT64_MAX >> 2);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Checks shared by the 2-D entry points.  W = out_mult * N is the output
+// width.  `blocked_cols` says whether the rowwise 32-blocks run along N.
+mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, int n_in, int64_t M,
+                      int64_t N, int layout, const void *q_row, int64_t ld_q_row, const void *s_row,
+                      int64_t ld_s_row, const void *q_col, int64_t ld_q_col, const void *s_col,
+                      int64_t ld_s_col) {
+  if (layout < MXFP8_ROWWISE || layout > MXFP8_BOTH) return MXFP8_ERR_LAYOUT;
+  if (M < 0 || N < 0) return MXFP8_ERR_SHAPE;
+  const bool rows = layout & MXFP8_ROWWISE, cols = layout & MXFP8_COLWISE;
+  if (kind != Kind::Quant && N % 32 != 0) return MXFP8_ERR_SHAPE;
+  if (kind == Kind::Quant && rows && N % 32 != 0) return MXFP8_ERR_SHAPE;
+  if (kind == Kind::Quant && N % 8 != 0) return MXFP8_ERR_SHAPE;
+  if (cols && M % 32 != 0) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  const int64_t W = (kind == Kind::Bwd ? 2 : 1) * N;
+  for (int j = 0; j < n_in; j++)
+    if (!in[j]) return MXFP8_ERR_NULL;
+  if (rows && (!q_row || !s_row)) return MXFP8_ERR_NULL;
+  if (cols && (!q_col || !s_col)) return MXFP8_ERR_NULL;
+  for (int j = 0; j < n_in; j++)
+    if (ld_in[j] < N || ld_in[j] % 8 != 0) return MXFP8_ERR_STRIDE;
+  if (rows && (ld_q_row < W || ld_q_row % 16 != 0 || ld_s_row < W / 32)) return MXFP8_ERR_STRIDE;
+  if (cols && (ld_q_col < M || ld_q_col % 16 != 0 || ld_s_col < M / 32)) return MXFP8_ERR_STRIDE;
+  for (int j = 0; j < n_in; j++)
+    if (!aligned16(in[j])) return MXFP8_ERR_ALIGN;
+  if (rows && !aligned16(q_row)) return MXFP8_ERR_ALIGN;
+  if (cols && !aligned16(q_col)) return MXFP8_ERR_ALIGN;
+  for (int j = 0; j < n_in; j++)
+    if (!extent_ok(M, N, ld_in[j])) return MXFP8_ERR_OVERFLOW;
+  if (rows && (!extent_ok(M, W, ld_q_row) || !extent_ok(M, W / 32, ld_s_row))) return MXFP8_ERR_OVERFLOW;
+  if (cols && (!extent_ok(W, M, ld_q_col) || !extent_ok(W, M / 32, ld_s_col))) return MXFP8_ERR_OVERFLOW;
+  return MXFP8_OK;
+}
+
+mxfp8_status launch(const void *kernel, int64_t blocks, const Args &a, void *stream) {
+  // Grid x is limited to 2^32 - 1 work-items; keep well inside it.
+  if (blocks <= 0 || blocks > (int64_t)INT32_MAX / 256) return MXFP8_ERR_OVERFLOW;
+  Args copy = a;
+  void *kargs[] = {&copy};
+  hipError_t err = hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(256), kargs, 0, (hipStream_t)stream);
+  return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
+#ifndef MX_COL_KERNEL
+#define MX_COL_KERNEL 0  // 1: register-resident strip kernel, 0: LDS-tiled kernel
+#endif
+
+// Launch of the colwise / both-layout kernel over `batches` stacked [M, N]
+// problems (batches > 1 only for the 3D cast).
+template <class Op>
+mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream) {
+#if MX_COL_KERNEL
+  const int64_t n_rt = (a.M + mx::kSM - 1) / mx::kSM, n_ct = (a.N + mx::kSC - 1) / mx::kSC;
+  if (n_rt > INT32_MAX || n_ct > INT32_MAX) return MXFP8_ERR_OVERFLOW;
+  // Split each row strip's columns into segments only when there are too
+  // few strips to fill the chip (about 2048 workgroups, 8 per CU).
+  int64_t strips;
+  if (!mul_ok(n_rt, batches, &strips)) return MXFP8_ERR_OVERFLOW;
+  int64_t n_seg = (2048 + strips - 1) / strips;
+  if (n_seg > n_ct) n_seg = n_ct;
+  if (n_seg < 1) n_seg = 1;
+  a.n_rt = (int32_t)n_rt;
+  a.n_ct = (int32_t)n_ct;
+  a.n_seg = (int32_t)n_seg;
+  int64_t blocks;
+  if (!mul_ok(strips, n_seg, &blocks)) return MXFP8_ERR_OVERFLOW;
+  const void *k = rows ? (const void *)&mx::k_strip<Op, true> : (const void *)&mx::k_strip<Op, false>;
+#else
+  const int64_t n_rt = (a.M + mx::kTM - 1) / mx::kTM, n_ct = (a.N + mx::kTC - 1) / mx::kTC;
+  if (n_rt > INT32_MAX || n_ct > INT32_MAX) return MXFP8_ERR_OVERFLOW;
+  a.n_rt = (int32_t)n_rt;
+  a.n_ct = (int32_t)n_ct;
+  int64_t blocks;
+  if (!mul_ok(n_rt, n_ct, &blocks) || !mul_ok(blocks, batches, &blocks)) return MXFP8_ERR_OVERFLOW;
+  const void *k = rows ? (const void *)&mx::k_tiled<Op, true> : (const void *)&mx::k_tiled<Op, false>;
+#endif
+  return launch(k, blocks, a, stream);
+}
+
+template <class Op>
+mxfp8_status dispatch_2d(const Args &a, int layout, void *stream) {
+  if (layout == MXFP8_ROWWISE) {
+    const int64_t blocks = (a.M + mx::kRowWaves - 1) / mx::kRowWaves;
+    return launch((const void *)&mx::k_rowwise<Op, kRowUnroll>, blocks, a, stream);
+  }
+  return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream);
+}
+
+Args make_args(const void *const *in, const int64_t *ld_in, int n_in, int64_t M, int64_t N, void *q_row,
+               int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col,
+               int64_t ld_s_col) {
+  Args a{};
+  for (int j = 0; j < n_in; j++) {
+    a.in[j] = static_cast<const uint16_t *>(in[j]);
+    a.ld_in[j] = ld_in[j];
+  }
+  a.M = M;
+  a.N = N;
+  a.q_row = static_cast<uint8_t *>(q_row);
+  a.ld_q_row = ld_q_row;
+  a.s_row = static_cast<uint8_t *>(s_row);
+  a.ld_s_row = ld_s_row;
+  a.q_col = static_cast<uint8_t *>(q_col);
+  a.ld_q_col = ld_q_col;
+  a.s_col = static_cast<uint8_t *>(s_col);
+  a.ld_s_col = ld_s_col;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp8_status mxfp8_swiglu_fwd(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
+                              int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
+                              int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                              void *stream) {
+  const void *in[2] = {gate, up};
+  const int64_t ld[2] = {ld_gate, ld_up};
+  mxfp8_status st = check_2d(Kind::Fwd, in, ld, 2, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
+                             ld_q_col, s_col, ld_s_col);
+  if (st != MXFP8_OK || M == 0 || N == 0) return st;
+  Args a = make_args(in, ld, 2, M, N, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
+  return dispatch_2d<mx::OpFwd>(a, layout, stream);
+}
+
+mxfp8_status mxfp8_swiglu_bwd(const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate, const void *up,
+                              int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row,
+                              void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col,
+                              int64_t ld_s_col, void *stream) {
+  const void *in[3] = {dh, gate, up};
+  const int64_t ld[3] = {ld_dh, ld_gate, ld_up};
+  mxfp8_status st = check_2d(Kind::Bwd, in, ld, 3, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
+                             ld_q_col, s_col, ld_s_col);
+  if (st != MXFP8_OK || M == 0 || N == 0) return st;
+  Args a = make_args(in, ld, 3, M, N, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
+  return dispatch_2d<mx::OpBwd>(a, layout, stream);
+}
+
+mxfp8_status mxfp8_quant_2d(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout, void *q_row,
+                            int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                            void *s_col, int64_t ld_s_col, void *stream) {
+  const void *in[1] = {x};
+  const int64_t ld[1] = {ld_x};
+  mxfp8_status st = check_2d(Kind::Quant, in, ld, 1, M, K, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
+                             ld_q_col, s_col, ld_s_col);
+  if (st != MXFP8_OK || M == 0 || K == 0) return st;
+  Args a = make_args(in, ld, 1, M, K, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
+  return dispatch_2d<mx::OpQuant>(a, layout, stream);
+}
+
+mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t K, int64_t stride_e,
+                                    int64_t ld_w, void *q, void *s, void *stream) {
+  if (E < 0 || N < 0 || K < 0) return MXFP8_ERR_SHAPE;
+  if (N % 32 != 0 || K % 8 != 0) return MXFP8_ERR_SHAPE;
+  if (E == 0 || N == 0 || K == 0) return MXFP8_OK;
+  if (!w || !q || !s) return MXFP8_ERR_NULL;
+  if (ld_w < K || ld_w % 8 != 0) return MXFP8_ERR_STRIDE;
+  int64_t slab;
+  if (!mul_ok(N, ld_w, &slab)) return MXFP8_ERR_OVERFLOW;
+  if (E > 1 && (stride_e < slab || stride_e % 8 != 0)) return MXFP8_ERR_STRIDE;
+  if (!aligned16(w) || !aligned16(q)) return MXFP8_ERR_ALIGN;
+  int64_t in_ext, out_ext;
+  if (!mul_ok(E - 1, stride_e, &in_ext) || !add_ok(in_ext, slab, &in_ext) || in_ext >= (INT64_MAX >> 2))
+    return MXFP8_ERR_OVERFLOW;
+  if (!mul_ok(E, N, &out_ext) || !mul_ok(out_ext, K, &out_ext) || out_ext >= (INT64_MAX >> 2))
+    return MXFP8_ERR_OVERFLOW;
+  const void *in[1] = {w};
+  const int64_t ld[1] = {ld_w};
+  // Expert e is a [N, K] matrix whose 32-blocks run down its N rows: the
+  // colwise cast with rows = N, columns = K, output rows of length N.
+  Args a = make_args(in, ld, 1, N, K, nullptr, 0, nullptr, 0, q, N, s, N / 32);
+  a.bstride_in = stride_e;
+  a.bstride_q = K * N;
+  a.bstride_s = K * (N / 32);
+  return launch_colwise<mx::OpQuant>(a, false, E, stream);
+}
+
+const char *mxfp8_status_str(mxfp8_status status) {
+  switch (status) {
+    case MXFP8_OK: return "ok";
+    case MXFP8_ERR_NULL: return "a required pointer is NULL";
+    case MXFP8_ERR_SHAPE: return "invalid shape (negative, or a blocked dimension not a multiple of 32)";
+    case MXFP8_ERR_STRIDE: return "invalid leading dimension (smaller than the row, or not a vector multiple)";
+    case MXFP8_ERR_ALIGN: return "input or E4M3 output pointer is not 16-byte aligned";
+    case MXFP8_ERR_LAYOUT: return "layout must be rowwise (1), colwise (2) or both (3)";
+    case MXFP8_ERR_OVERFLOW: return "sizes overflow the addressable range or the launch grid";
+    case MXFP8_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

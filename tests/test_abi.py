@@ -1,0 +1,165 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry
+point, and every argument check returns its status before any HIP call.
+
+Mirrors the launcher guards of "Add swiglu + MXFP8 fused CuTe DSL kernel"
+(Numerics and tests: each error path exercised without allocating).  Every
+call below is invalid or empty, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import swiglu_activation_cast_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, STRIDE, ALIGN, LAYOUT, OVERFLOW, LAUNCH = range(8)
+
+A = 1 << 20  # a fake, 16-byte aligned "device address" (never dereferenced)
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "mxfp8.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(mxfp8_\w+)\s*\(", text))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mx.lib()
+    names = declared_functions()
+    assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_quant_2d", "mxfp8_quant_3d_colwise",
+                     "mxfp8_status_str"}
+    for n in names:
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings():
+    for st in range(8):
+        assert len(mx.status_str(st)) >= 2
+    assert mx.status_str(99) == "unknown status"
+
+
+def fwd(**kw):
+    a = dict(gate=A, ld_gate=256, up=A + 256, ld_up=256, M=64, N=128, layout=3,
+             q_row=A, ld_q_row=128, s_row=A, ld_s_row=4, q_col=A, ld_q_col=64, s_col=A, ld_s_col=2)
+    a.update(kw)
+    return mx.lib().mxfp8_swiglu_fwd(a["gate"], a["ld_gate"], a["up"], a["ld_up"], a["M"], a["N"], a["layout"],
+                                     a["q_row"], a["ld_q_row"], a["s_row"], a["ld_s_row"], a["q_col"],
+                                     a["ld_q_col"], a["s_col"], a["ld_s_col"], None)
+
+
+def bwd(**kw):
+    a = dict(dh=A, ld_dh=128, gate=A, ld_gate=256, up=A + 256, ld_up=256, M=64, N=128, layout=3,
+             q_row=A, ld_q_row=256, s_row=A, ld_s_row=8, q_col=A, ld_q_col=64, s_col=A, ld_s_col=2)
+    a.update(kw)
+    return mx.lib().mxfp8_swiglu_bwd(a["dh"], a["ld_dh"], a["gate"], a["ld_gate"], a["up"], a["ld_up"], a["M"],
+                                     a["N"], a["layout"], a["q_row"], a["ld_q_row"], a["s_row"], a["ld_s_row"],
+                                     a["q_col"], a["ld_q_col"], a["s_col"], a["ld_s_col"], None)
+
+
+def q2d(**kw):
+    a = dict(x=A, ld_x=128, M=64, K=128, layout=3, q_row=A, ld_q_row=128, s_row=A, ld_s_row=4, q_col=A,
+             ld_q_col=64, s_col=A, ld_s_col=2)
+    a.update(kw)
+    return mx.lib().mxfp8_quant_2d(a["x"], a["ld_x"], a["M"], a["K"], a["layout"], a["q_row"], a["ld_q_row"],
+                                   a["s_row"], a["ld_s_row"], a["q_col"], a["ld_q_col"], a["s_col"], a["ld_s_col"],
+                                   None)
+
+
+def q3d(**kw):
+    a = dict(w=A, E=4, N=64, K=40, stride_e=64 * 40, ld_w=40, q=A, s=A)
+    a.update(kw)
+    return mx.lib().mxfp8_quant_3d_colwise(a["w"], a["E"], a["N"], a["K"], a["stride_e"], a["ld_w"], a["q"], a["s"],
+                                           None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, q2d])
+def test_layout_errors(call):
+    for layout in (0, 4, -1, 7):
+        assert call(layout=layout) == LAYOUT
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_swiglu_shape_errors(call):
+    assert call(M=-1) == SHAPE
+    assert call(N=-32) == SHAPE
+    assert call(N=48) == SHAPE                     # width not a multiple of 32
+    assert call(M=40, layout=2) == SHAPE           # colwise rows not a multiple of 32
+    assert call(M=40, layout=3) == SHAPE
+
+
+def test_quant_2d_shape_errors():
+    assert q2d(K=40, layout=1) == SHAPE            # rowwise blocks run along K
+    assert q2d(K=36, layout=2, ld_x=40) == SHAPE   # colwise needs K % 8 == 0
+    assert q2d(M=33, layout=2) == SHAPE
+
+
+@pytest.mark.parametrize("call", [fwd, bwd, q2d])
+def test_empty_is_ok_without_pointers(call):
+    nul = dict(q_row=None, s_row=None, q_col=None, s_col=None)
+    if call is q2d:
+        assert call(M=0, x=None, **nul) == OK
+        assert call(K=0, x=None, **nul) == OK
+    else:
+        assert call(M=0, gate=None, up=None, **nul) == OK
+        assert call(N=0, gate=None, up=None, **nul) == OK
+
+
+def test_null_errors():
+    assert fwd(gate=None) == NULL
+    assert fwd(up=None) == NULL
+    assert fwd(q_row=None) == NULL
+    assert fwd(s_col=None) == NULL
+    assert bwd(dh=None) == NULL
+    assert q2d(x=None) == NULL
+    assert q2d(s_row=None, layout=1) == NULL
+    # pointers of a layout that is not requested may be NULL; the call then
+    # fails later on purpose (bad stride) so that nothing launches
+    assert fwd(q_col=None, s_col=None, layout=1, ld_gate=100) == STRIDE
+
+
+def test_stride_errors():
+    assert fwd(ld_gate=64) == STRIDE               # smaller than N
+    assert fwd(ld_up=132) == STRIDE                # not a multiple of 8 elements
+    assert fwd(ld_q_row=120) == STRIDE             # smaller than W
+    assert fwd(ld_q_row=136) == STRIDE             # not a multiple of 16 bytes
+    assert fwd(ld_s_row=3) == STRIDE
+    assert fwd(ld_q_col=40) == STRIDE              # smaller than M
+    assert fwd(ld_s_col=1) == STRIDE
+    assert bwd(ld_q_row=128) == STRIDE             # W = 2N = 256
+    assert bwd(ld_s_row=4) == STRIDE
+    assert bwd(ld_dh=120) == STRIDE
+
+
+def test_alignment_errors():
+    assert fwd(gate=A + 2) == ALIGN
+    assert fwd(up=A + 8) == ALIGN
+    assert fwd(q_row=A + 4) == ALIGN
+    assert fwd(q_col=A + 1) == ALIGN
+    assert bwd(dh=A + 2) == ALIGN
+    assert q2d(x=A + 6) == ALIGN
+    # scale pointers have no alignment requirement: the call proceeds to the
+    # next check (made to fail here so that nothing launches)
+    assert fwd(s_row=A + 1, ld_gate=100) == STRIDE
+
+
+def test_overflow_errors():
+    big = 1 << 61
+    assert fwd(M=big, ld_gate=big) == OVERFLOW or fwd(M=big, ld_gate=big) == STRIDE
+    assert q2d(M=1 << 40, K=1 << 24, ld_x=1 << 24, ld_q_row=1 << 24, ld_s_row=1 << 19, layout=1) == OVERFLOW
+
+
+def test_3d_errors():
+    assert q3d(E=-1) == SHAPE
+    assert q3d(N=48) == SHAPE
+    assert q3d(K=36, ld_w=40) == SHAPE
+    assert q3d(E=0, w=None, q=None, s=None) == OK
+    assert q3d(w=None) == NULL
+    assert q3d(q=None) == NULL
+    assert q3d(ld_w=36) == STRIDE
+    assert q3d(ld_w=44) == STRIDE
+    assert q3d(stride_e=64 * 40 - 8) == STRIDE
+    assert q3d(w=A + 2) == ALIGN
+    assert q3d(q=A + 8) == ALIGN
+    assert q3d(E=1 << 40, stride_e=1 << 30) == OVERFLOW

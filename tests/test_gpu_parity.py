@@ -1,0 +1,408 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle.
+
+Quant-only casts (2D and 3D) must be bit-exact.  Fused SwiGLU casts follow
+the tolerance in tests/parity.py.  Inputs come from the seeded generators in
+swiglu_activation_cast_amd.synth (or are built explicitly for edge cases);
+the oracle reads back the exact device bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import swiglu_activation_cast_amd as mx
+from swiglu_activation_cast_amd import synth
+from helpers import all_bf16_bits, bits_to_torch_bf16, torch_bf16_to_bits
+from parity import assert_exact, compare_fused
+
+pytestmark = pytest.mark.gpu
+
+ROW, COL, BOTH = 1, 2, 3
+LAYOUTS = (ROW, COL, BOTH)
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def _gpu(outs):
+    """Binding order (q_row, q_col, s_row, s_col) -> oracle order (q_row, s_row, q_col, s_col)."""
+    q_row, q_col, s_row, s_col = outs
+    return _np(q_row), _np(s_row), _np(q_col), _np(s_col)
+
+
+def _flags(layout):
+    return dict(rowwise=bool(layout & ROW), colwise=bool(layout & COL))
+
+
+def _to_dev(bits, dev):
+    return bits_to_torch_bf16(bits).to(dev)
+
+
+def _exact(name, gpu, orc, layout):
+    if layout & ROW:
+        assert_exact(name + "/q_row", gpu[0], orc[0])
+        assert_exact(name + "/s_row", gpu[1], orc[1])
+    if layout & COL:
+        assert_exact(name + "/q_col", gpu[2], orc[2])
+        assert_exact(name + "/s_col", gpu[3], orc[3])
+
+
+def _fwd_check(oracle_mod, name, g_bits, u_bits, layout, dev):
+    g, u = _to_dev(g_bits, dev), _to_dev(u_bits, dev)
+    gpu = _gpu(mx.mxfp8_swiglu_fwd(g, u, **_flags(layout)))
+    orc = oracle_mod.swiglu_fwd(g_bits, u_bits, layout)
+    vals = oracle_mod.swiglu_fwd_values(np.ascontiguousarray(g_bits), np.ascontiguousarray(u_bits))
+    return compare_fused(oracle_mod, name, gpu, orc, vals, layout)
+
+
+def _bwd_check(oracle_mod, name, dh_bits, g_bits, u_bits, layout, dev):
+    dh, g, u = _to_dev(dh_bits, dev), _to_dev(g_bits, dev), _to_dev(u_bits, dev)
+    gpu = _gpu(mx.mxfp8_swiglu_bwd(dh, g, u, **_flags(layout)))
+    orc = oracle_mod.swiglu_bwd(dh_bits, g_bits, u_bits, layout)
+    dg, du = oracle_mod.swiglu_bwd_values(*(np.ascontiguousarray(a) for a in (dh_bits, g_bits, u_bits)))
+    vals = np.concatenate([dg, du], axis=1)
+    return compare_fused(oracle_mod, name, gpu, orc, vals, layout)
+
+
+# ------------------------------------------------------------ quant-only, exact
+def test_quant_2d_all_bf16_patterns(oracle_mod):
+    dev = _dev()
+    print("case: quant_2d all bf16 patterns [2048, 32]", flush=True)
+    rng = np.random.default_rng(0)
+    x = rng.permutation(all_bf16_bits()).reshape(2048, 32)
+    gpu = _gpu(mx.mxfp8_quant_2d(_to_dev(x, dev), rowwise=True, colwise=True))
+    _exact("all_patterns", gpu, oracle_mod.quant_2d(x, BOTH), BOTH)
+
+
+def test_quant_2d_every_value_under_many_scales(oracle_mod):
+    """Each block: one driver element at 448 * 2^k (fixing the scale to byte
+    127 + k) and 31 finite bf16 values of smaller magnitude, covering every
+    such value once per chosen k."""
+    dev = _dev()
+    bits = all_bf16_bits()
+    mag = bits & 0x7FFF
+    rng = np.random.default_rng(1)
+    for k in (-127, -126, -100, -8, 0, 5, 60, 119, 120):
+        print(f"case: quant_2d value sweep at scale byte {127 + k}", flush=True)
+        # 448 * 2^120 overflows bf16: the largest finite bf16 drives byte 247
+        driver = oracle_mod.bf16_round(448.0 * 2.0**k) if k < 120 else 0x7F7F
+        pool = bits[(mag < 0x7F80) & (mag <= (driver & 0x7FFF))]
+        pool = rng.permutation(pool)
+        nblk = -(-pool.size // 31)
+        body = np.resize(pool, nblk * 31).reshape(nblk, 31)
+        x = np.concatenate([np.full((nblk, 1), driver, np.uint16), body], axis=1)
+        gpu = _gpu(mx.mxfp8_quant_2d(_to_dev(x, dev), rowwise=True, colwise=False))
+        orc = oracle_mod.quant_2d(x, ROW)
+        assert (orc[1][:, 0] == 127 + k).all()
+        _exact(f"sweep{k}", gpu, orc, ROW)
+
+
+@pytest.mark.parametrize("M,K,layout", [(37, 96, ROW), (96, 40, COL), (160, 224, BOTH), (128, 64, COL),
+                                        (32, 8, COL), (1, 32, ROW), (224, 1056, BOTH)])
+def test_quant_2d_shapes(oracle_mod, M, K, layout):
+    dev = _dev()
+    print(f"case: quant_2d M={M} K={K} layout={layout}", flush=True)
+    x = torch_bf16_to_bits(synth.normal_bf16((M, K), 2.0, seed=M * 7 + K))
+    gpu = _gpu(mx.mxfp8_quant_2d(_to_dev(x, dev), **_flags(layout)))
+    _exact(f"shape{M}x{K}", gpu, oracle_mod.quant_2d(x, layout), layout)
+
+
+def test_quant_2d_strided_input(oracle_mod):
+    dev = _dev()
+    big = torch_bf16_to_bits(synth.normal_bf16((96, 320), 1.0, seed=5))
+    x_dev = _to_dev(big, dev)[:, 64:256]  # ld = 320
+    gpu = _gpu(mx.mxfp8_quant_2d(x_dev, rowwise=True, colwise=True))
+    _exact("strided", gpu, oracle_mod.quant_2d(big[:, 64:256], BOTH), BOTH)
+
+
+def test_quant_2d_e4m3_boundary_amax(oracle_mod):
+    """amax exactly 448 * 2^k and one bf16 step either side."""
+    dev = _dev()
+    rows = []
+    rng = np.random.default_rng(2)
+    for k in range(-127, 121, 3):
+        b = oracle_mod.bf16_round(448.0 * 2.0**k)
+        for a in (b - 1, b, b + 1):
+            row = np.zeros(32, np.uint16)
+            row[:] = rng.integers(0, max(1, a), 32)
+            row[rng.integers(0, 32)] = a | (0x8000 if rng.random() < 0.5 else 0)
+            rows.append(row)
+    x = np.stack(rows)
+    x = x[: len(x) // 32 * 32]
+    gpu = _gpu(mx.mxfp8_quant_2d(_to_dev(x, dev), rowwise=True, colwise=True))
+    _exact("boundary", gpu, oracle_mod.quant_2d(x, BOTH), BOTH)
+
+
+# ---------------------------------------------------------------- fused, small
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_swiglu_fwd_128x128(oracle_mod, layout):
+    dev = _dev()
+    print(f"case: fwd 128x128 seed 0 layout={layout}", flush=True)
+    inp = synth.workload("swiglu_128x128")
+    _fwd_check(oracle_mod, f"fwd128/{layout}", torch_bf16_to_bits(inp.gate), torch_bf16_to_bits(inp.up), layout, dev)
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_swiglu_bwd_128x128(oracle_mod, layout):
+    dev = _dev()
+    print(f"case: bwd 128x128 seed 0 layout={layout}", flush=True)
+    inp = synth.workload("swiglu_128x128")
+    _bwd_check(oracle_mod, f"bwd128/{layout}", torch_bf16_to_bits(inp.dh), torch_bf16_to_bits(inp.gate),
+               torch_bf16_to_bits(inp.up), layout, dev)
+
+
+@pytest.mark.parametrize("M,N,layout", [(37, 64, ROW), (96, 96, COL), (160, 224, BOTH), (64, 1056, BOTH)])
+def test_swiglu_ragged_shapes(oracle_mod, M, N, layout):
+    dev = _dev()
+    print(f"case: fwd/bwd ragged M={M} N={N} layout={layout}", flush=True)
+    inp = synth.swiglu_inputs(M, N, seed=M + N, std=2.0)
+    g, u, dh = (torch_bf16_to_bits(t) for t in (inp.gate, inp.up, inp.dh))
+    _fwd_check(oracle_mod, f"fwd{M}x{N}", g, u, layout, dev)
+    _bwd_check(oracle_mod, f"bwd{M}x{N}", dh, g, u, layout, dev)
+
+
+# ------------------------------------------------------ fused, 4096 x 2048 full
+@pytest.fixture(scope="module")
+def c2_inputs():
+    inp = synth.workload("swiglu_4096x2048_outliers")
+    return tuple(torch_bf16_to_bits(t) for t in (inp.gate, inp.up, inp.dh))
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_swiglu_fwd_4096x2048_outliers(oracle_mod, c2_inputs, layout):
+    dev = _dev()
+    print(f"case: fwd 4096x2048 outliers layout={layout}", flush=True)
+    g, u, _ = c2_inputs
+    st = _fwd_check(oracle_mod, f"fwdC2/{layout}", g, u, layout, dev)
+    print(f"  blocks={st.blocks} scale_mismatch={st.scale_mismatch} off_by_one={st.code_off_by_one}")
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_swiglu_bwd_4096x2048_outliers(oracle_mod, c2_inputs, layout):
+    dev = _dev()
+    print(f"case: bwd 4096x2048 outliers layout={layout}", flush=True)
+    g, u, dh = c2_inputs
+    st = _bwd_check(oracle_mod, f"bwdC2/{layout}", dh, g, u, layout, dev)
+    print(f"  blocks={st.blocks} scale_mismatch={st.scale_mismatch} off_by_one={st.code_off_by_one}")
+
+
+def test_cross_mode_bitwise(c2_inputs):
+    """Both-mode output equals the rowwise-only and colwise-only outputs."""
+    dev = _dev()
+    g, u, dh = (_to_dev(a, dev) for a in c2_inputs)
+    for name, fn, args in (("quant", mx.mxfp8_quant_2d, (g,)), ("fwd", mx.mxfp8_swiglu_fwd, (g, u)),
+                           ("bwd", mx.mxfp8_swiglu_bwd, (dh, g, u))):
+        both = fn(*args, rowwise=True, colwise=True)
+        row = fn(*args, rowwise=True, colwise=False)
+        col = fn(*args, rowwise=False, colwise=True)
+        assert torch.equal(both[0], row[0]) and torch.equal(both[2], row[2]), name
+        assert torch.equal(both[1], col[1]) and torch.equal(both[3], col[3]), name
+
+
+# -------------------------------------------------------------- edge values
+def test_far_negative_gates(oracle_mod):
+    """Whole blocks of gates in [-98, -80]: silu is a tiny (often subnormal)
+    negative number, not -0."""
+    dev = _dev()
+    rng = np.random.default_rng(3)
+    M, N = 64, 128
+    g = torch.from_numpy(rng.uniform(-98, -80, (M, N))).to(torch.bfloat16)
+    u = torch.from_numpy(rng.standard_normal((M, N))).to(torch.bfloat16)
+    dh = torch.from_numpy(rng.standard_normal((M, N))).to(torch.bfloat16)
+    g, u, dh = (torch_bf16_to_bits(t) for t in (g, u, dh))
+    for layout in LAYOUTS:
+        _fwd_check(oracle_mod, f"far_fwd/{layout}", g, u, layout, dev)
+        _bwd_check(oracle_mod, f"far_bwd/{layout}", dh, g, u, layout, dev)
+
+
+def test_special_values(oracle_mod):
+    """NaN/Inf in any input, all-zero blocks, bf16 subnormals, huge gates."""
+    dev = _dev()
+    rng = np.random.default_rng(4)
+    M, N = 96, 160
+    g, u, dh = (torch_bf16_to_bits(torch.from_numpy(rng.standard_normal((M, N)) * 3).to(torch.bfloat16))
+                for _ in range(3))
+    g[0, 3] = 0x7FC0
+    u[5, 40] = 0x7F80
+    dh[9, 100] = 0xFF80
+    g[40, 70] = 0xFF80          # -Inf gate
+    g[41, 71] = 0x7F80          # +Inf gate
+    g[64:96, 0:32] = 0          # all-zero blocks in both layouts
+    u[64:96, 32:64] = rng.integers(1, 0x7F, (32, 32))  # subnormal up
+    g[10:12, 128:160] = rng.integers(1, 0x7F, (2, 32)).astype(np.uint16) | 0x8000  # subnormal gates
+    g[20, 130:140] = 0x4400     # 512
+    g[21, 130:140] = 0xC400     # -512
+    for layout in LAYOUTS:
+        _fwd_check(oracle_mod, f"special_fwd/{layout}", g, u, layout, dev)
+        _bwd_check(oracle_mod, f"special_bwd/{layout}", dh, g, u, layout, dev)
+
+
+def test_exhaustive_gate_values(oracle_mod):
+    """Every finite bf16 gate once (u = 1, dh = 1): the fp32 activation's
+    distance from the exact one, over the whole gate range."""
+    dev = _dev()
+    bits = all_bf16_bits()
+    fin = bits[(bits & 0x7FFF) < 0x7F80]
+    fin = np.resize(fin, (fin.size // (32 * 64) + 1) * 32 * 64).reshape(-1, 64)
+    one = np.full_like(fin, 0x3F80)
+    st = _fwd_check(oracle_mod, "all_gates_fwd", fin, one, BOTH, dev)
+    st2 = _bwd_check(oracle_mod, "all_gates_bwd", one, fin, one, BOTH, dev)
+    print(f"  fwd off_by_one={st.code_off_by_one} bwd off_by_one={st2.code_off_by_one} of {st.elements}")
+
+
+# ------------------------------------------------ full-size, sampled slabs
+def _slabs(M, n, seed):
+    rng = np.random.default_rng(seed)
+    picks = {0, M // 32 - 1} | set(rng.integers(0, M // 32, n).tolist())
+    return sorted(picks)
+
+
+def _check_sampled(oracle_mod, name, inp, layout, slabs, bwd):
+    M, N = inp.gate.shape
+    fn = mx.mxfp8_swiglu_bwd if bwd else mx.mxfp8_swiglu_fwd
+    args = (inp.dh, inp.gate, inp.up) if bwd else (inp.gate, inp.up)
+    outs = fn(*args, **_flags(layout))
+    q_row, q_col, s_row, s_col = outs
+    torch.cuda.synchronize()
+    for sb in slabs:
+        r0, r1 = sb * 32, sb * 32 + 32
+        host = [torch_bf16_to_bits(a[r0:r1]) for a in args]
+        gpu = (_np(q_row[r0:r1]) if layout & ROW else None, _np(s_row[r0:r1]) if layout & ROW else None,
+               _np(q_col[:, r0:r1]) if layout & COL else None, _np(s_col[:, sb:sb + 1]) if layout & COL else None)
+        if bwd:
+            orc = oracle_mod.swiglu_bwd(*host, layout)
+            dg, du = oracle_mod.swiglu_bwd_values(*host)
+            vals = np.concatenate([dg, du], axis=1)
+        else:
+            orc = oracle_mod.swiglu_fwd(*host, layout)
+            vals = oracle_mod.swiglu_fwd_values(*host)
+        compare_fused(oracle_mod, f"{name}/slab{sb}", gpu, orc, vals, layout)
+    return outs
+
+
+def test_swiglu_16384x7168_w13_sampled(oracle_mod):
+    dev = _dev()
+    print("case: 16384x7168 w13, both layouts, sampled slabs", flush=True)
+    inp = synth.workload("swiglu_16384x7168_w13", device=dev)
+    slabs = _slabs(16384, 4, 11)
+    both_f = _check_sampled(oracle_mod, "fwdC3", inp, BOTH, slabs, bwd=False)
+    both_b = _check_sampled(oracle_mod, "bwdC3", inp, BOTH, slabs, bwd=True)
+    # the single-layout launches agree bitwise with the both-layout one
+    for fn, args, ref in ((mx.mxfp8_swiglu_fwd, (inp.gate, inp.up), both_f),
+                          (mx.mxfp8_swiglu_bwd, (inp.dh, inp.gate, inp.up), both_b)):
+        row = fn(*args, rowwise=True, colwise=False)
+        assert torch.equal(row[0], ref[0]) and torch.equal(row[2], ref[2])
+        del row
+        col = fn(*args, rowwise=False, colwise=True)
+        assert torch.equal(col[1], ref[1]) and torch.equal(col[3], ref[3])
+        del col
+
+
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_swiglu_131072x8192_w13_sampled(oracle_mod, layout):
+    dev = _dev()
+    print(f"case: 131072x8192 w13 layout={layout}, sampled slabs", flush=True)
+    inp = synth.workload("swiglu_131072x8192_w13", device=dev)
+    slabs = _slabs(131072, 3, 12 + layout)
+    _check_sampled(oracle_mod, f"fwdC5/{layout}", inp, layout, slabs, bwd=False)
+    torch.cuda.empty_cache()
+    _check_sampled(oracle_mod, f"bwdC5/{layout}", inp, layout, slabs, bwd=True)
+    del inp
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------- 3D
+def test_quant_3d_small_shapes(oracle_mod):
+    dev = _dev()
+    for E, N, K in ((1, 32, 8), (3, 96, 40), (2, 160, 200), (5, 64, 64)):
+        print(f"case: 3d E={E} N={N} K={K}", flush=True)
+        w = torch_bf16_to_bits(synth.expert_weights(E, N, K, seed=E * N + K, std=0.5))
+        q, s = mx.mxfp8_quant_3d_colwise(_to_dev(w.reshape(E * N, K), dev).reshape(E, N, K))
+        qo, so = oracle_mod.quant_3d_colwise(w)
+        assert_exact("q3d", _np(q), qo)
+        assert_exact("s3d", _np(s), so)
+
+
+def test_quant_3d_strided_experts(oracle_mod):
+    dev = _dev()
+    big = torch_bf16_to_bits(synth.expert_weights(3, 100, 72, seed=9, std=1.0))
+    w_dev = _to_dev(big.reshape(300, 72), dev).reshape(3, 100, 72)[:, 4:68, 8:56]  # stride_e 7200, ld 72
+    q, s = mx.mxfp8_quant_3d_colwise(w_dev)
+    qo, so = oracle_mod.quant_3d_colwise(big[:, 4:68, 8:56])
+    assert_exact("q3d_strided", _np(q), qo)
+    assert_exact("s3d_strided", _np(s), so)
+
+
+@pytest.mark.parametrize("E", [1, 4, 64])
+def test_quant_3d_experts_8192x5120(oracle_mod, E):
+    """Full expert stacks: every expert against the 2D colwise kernel
+    (bitwise), sampled K columns of sampled experts against the oracle."""
+    dev = _dev()
+    print(f"case: 3d E={E} 8192x5120", flush=True)
+    w = synth.expert_workload(E, device=dev)
+    q, s = mx.mxfp8_quant_3d_colwise(w)
+    rng = np.random.default_rng(E)
+    experts = sorted({0, E - 1} | set(rng.integers(0, E, 2).tolist()))
+    for e in experts:
+        _, q2, _, s2 = mx.mxfp8_quant_2d(w[e], rowwise=False, colwise=True)
+        assert torch.equal(q[e], q2) and torch.equal(s[e], s2), e
+        k0 = int(rng.integers(0, 5120 // 64)) * 64
+        host = torch_bf16_to_bits(w[e][:, k0:k0 + 64])
+        qo, so = oracle_mod.quant_3d_colwise(host.reshape(1, 8192, 64))
+        assert_exact(f"q3d_e{e}", _np(q[e, k0:k0 + 64]), qo[0])
+        assert_exact(f"s3d_e{e}", _np(s[e, k0:k0 + 64]), so[0])
+    del w, q, s
+    torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------- bounds and contract
+def test_guard_bytes_and_padding_untouched():
+    """Outputs carved out of larger 0xA5-filled buffers with padded leading
+    dimensions: only the result bytes change."""
+    dev = _dev()
+    M, N = 96, 160
+    inp = synth.swiglu_inputs(M, N, seed=21, device=dev)
+    pad = 4096
+    for fn, args, W in ((mx.mxfp8_swiglu_fwd, (inp.gate, inp.up), N),
+                        (mx.mxfp8_swiglu_bwd, (inp.dh, inp.gate, inp.up), 2 * N)):
+        ldq_r, lds_r, ldq_c, lds_c = W + 32, W // 32 + 5, M + 48, M // 32 + 3
+        shapes = ((M, ldq_r), (M, lds_r), (W, ldq_c), (W, lds_c))
+        bufs = [torch.full((pad * 2 + r * c,), 0xA5, dtype=torch.uint8, device=dev) for r, c in shapes]
+        views = [b[pad:pad + r * c].view(r, c) for b, (r, c) in zip(bufs, shapes)]
+        outs = (views[0][:, :W], views[2][:, :M], views[1][:, :W // 32], views[3][:, :M // 32])
+        ref = fn(*args, rowwise=True, colwise=True)
+        fn(*args, rowwise=True, colwise=True, out=outs)
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r)
+        for b, v, (r, c), used in zip(bufs, views, shapes, (W, W // 32, M, M // 32)):
+            assert (b[:pad] == 0xA5).all() and (b[pad + r * c:] == 0xA5).all()
+            assert (v[:, used:] == 0xA5).all()
+
+
+def test_misaligned_and_bad_shapes_raise():
+    dev = _dev()
+    x = torch.zeros((64, 72), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(mx.Mxfp8Error) as ei:
+        mx.mxfp8_quant_2d(x[:, 1:65], rowwise=True)  # pointer 2 bytes past a 16-byte boundary
+    assert ei.value.status == 4
+    with pytest.raises(mx.Mxfp8Error) as ei:
+        mx.mxfp8_swiglu_fwd(x[:, :48], x[:, :48])  # width not a multiple of 32
+    assert ei.value.status == 2
+    with pytest.raises(mx.Mxfp8Error) as ei:
+        mx.mxfp8_quant_2d(x[:40, :64], colwise=True, rowwise=False)  # rows not a multiple of 32
+    assert ei.value.status == 2
+
+
+def test_empty_inputs_are_noops():
+    dev = _dev()
+    x = torch.zeros((0, 64), dtype=torch.bfloat16, device=dev)
+    outs = mx.mxfp8_swiglu_fwd(x, x, rowwise=True, colwise=True)
+    assert outs[0].shape == (0, 64) and outs[1].shape == (64, 0)
+    q, s = mx.mxfp8_quant_3d_colwise(torch.zeros((0, 32, 8), dtype=torch.bfloat16, device=dev))
+    assert q.numel() == 0 and s.numel() == 0
