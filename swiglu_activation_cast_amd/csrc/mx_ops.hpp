@@ -21,83 +21,77 @@ struct OpQuant {
   __device__ __forceinline__ static void apply(const V4 *in, V4 *out) { out[0] = in[0]; }
 };
 
+// A gate below -80 needs the scaled sigmoid (see mx_device.hpp).  In bf16,
+// g < -80 exactly when the 16-bit pattern, read unsigned, exceeds 0xC2A0
+// (sign set, magnitude above 80); negative NaNs also land here, which is
+// harmless because the careful path propagates NaN too.
+__device__ __forceinline__ bool any_far(const u32 *g) {
+  u32 m = pk_max(pk_max(g[0], g[1]), pk_max(g[2], g[3]));
+  return max(m & 0xffffu, m >> 16) > 0xC2A0u;
+}
+
+// silu(g) in fp32.  `careful` handles gates below -80 through e^g * 2^64.
+template <bool careful>
+__device__ __forceinline__ float silu_f(float g) {
+  float s = g * sigmoid_near(g);
+  if (careful && g < kFar) s = (g * exp_g_times_2p64(g)) * k2m64;
+  return s;
+}
+
 struct OpFwd {
   static constexpr int IN = 2, OUT = 1;  // in: gate, up
+
+  template <bool careful>
+  __device__ __forceinline__ static void eval(const u32 *g, const u32 *u, u32 *h) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      u32 sp = pack_bf16(silu_f<careful>(lo_f(g[k])), silu_f<careful>(hi_f(g[k])));
+      h[k] = pack_bf16(lo_f(sp) * lo_f(u[k]), hi_f(sp) * hi_f(u[k]));
+    }
+  }
+
   __device__ __forceinline__ static void apply(const V4 *in, V4 *out) {
     const u32 *g = &in[0].x, *u = &in[1].x;
     u32 *h = &out[0].x;
-    float s[8];
-    bool far = false;
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      float g0 = lo_f(g[k]), g1 = hi_f(g[k]);
-      s[2 * k] = g0 * sigmoid_near(g0);
-      s[2 * k + 1] = g1 * sigmoid_near(g1);
-      far |= (g0 < kFar) | (g1 < kFar);
-    }
-    if (__builtin_expect(far, 0)) {
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        float gk = (k & 1) ? hi_f(g[k >> 1]) : lo_f(g[k >> 1]);
-        if (gk < kFar) s[k] = (gk * exp_g_times_2p64(gk)) * k2m64;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      u32 sp = pack_bf16(s[2 * k], s[2 * k + 1]);
-      h[k] = pack_bf16(lo_f(sp) * lo_f(u[k]), hi_f(sp) * hi_f(u[k]));
-    }
+    eval<false>(g, u, h);
+    // rare: redo the whole chunk from the packed inputs, so only packed
+    // words are live across the branch
+    if (__builtin_expect(any_far(g), 0)) eval<true>(g, u, h);
   }
 };
 
 struct OpBwd {
   static constexpr int IN = 3, OUT = 2;  // in: dh, gate, up; out: dgate, dup
+
+  template <bool careful>
+  __device__ __forceinline__ static void elem(float dhv, float gv, float uv, float &dg, float &du) {
+    const float sig = sigmoid_near(gv);
+    const float s = round_bf16(silu_f<careful>(gv));
+    du = dhv * s;
+    const float ds = round_bf16(dhv * uv);
+    float r = (ds * sig) * (1.0f + gv * (1.0f - sig));
+    // far-negative gate: sig == e^g, so dg = ds * e^g * (1 + g); 2^-64 last
+    if (careful && gv < kFar) r = ((ds * (1.0f + gv)) * exp_g_times_2p64(gv)) * k2m64;
+    dg = r;
+  }
+
+  template <bool careful>
+  __device__ __forceinline__ static void eval(const u32 *dh, const u32 *g, const u32 *u, u32 *dg, u32 *du) {
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      float g0, u0, g1, u1;
+      elem<careful>(lo_f(dh[k]), lo_f(g[k]), lo_f(u[k]), g0, u0);
+      elem<careful>(hi_f(dh[k]), hi_f(g[k]), hi_f(u[k]), g1, u1);
+      dg[k] = pack_bf16(g0, g1);
+      du[k] = pack_bf16(u0, u1);
+    }
+  }
+
   __device__ __forceinline__ static void apply(const V4 *in, V4 *out) {
     const u32 *dh = &in[0].x, *g = &in[1].x, *u = &in[2].x;
     u32 *dg = &out[0].x, *du = &out[1].x;
-    float sig[8], s[8], gv[8];
-    bool far = false;
-#pragma unroll
-    for (int k = 0; k < 8; k++) {
-      gv[k] = (k & 1) ? hi_f(g[k >> 1]) : lo_f(g[k >> 1]);
-      sig[k] = sigmoid_near(gv[k]);
-      s[k] = gv[k] * sig[k];
-      far |= gv[k] < kFar;
-    }
-    float e[8];  // e^g * 2^64 for far-negative gates
-    if (__builtin_expect(far, 0)) {
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        e[k] = exp_g_times_2p64(gv[k]);
-        if (gv[k] < kFar) s[k] = (gv[k] * e[k]) * k2m64;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 4; k++) {
-      float dh0 = lo_f(dh[k]), dh1 = hi_f(dh[k]);
-      u32 sp = pack_bf16(s[2 * k], s[2 * k + 1]);
-      du[k] = pack_bf16(dh0 * lo_f(sp), dh1 * hi_f(sp));
-      u32 dsp = pack_bf16(dh0 * lo_f(u[k]), dh1 * hi_f(u[k]));
-      float ds0 = lo_f(dsp), ds1 = hi_f(dsp);
-      float a0 = sig[2 * k], a1 = sig[2 * k + 1];
-      float r0 = (ds0 * a0) * (1.0f + gv[2 * k] * (1.0f - a0));
-      float r1 = (ds1 * a1) * (1.0f + gv[2 * k + 1] * (1.0f - a1));
-      dg[k] = pack_bf16(r0, r1);
-    }
-    if (__builtin_expect(far, 0)) {
-      // sig == e^g here, so dg = ds * e^g * (1 + g); the 2^-64 goes last.
-#pragma unroll
-      for (int k = 0; k < 8; k++) {
-        if (gv[k] < kFar) {
-          float ds = (k & 1) ? hi_f(pack_bf16(0.0f, hi_f(dh[k >> 1]) * hi_f(u[k >> 1])))
-                             : lo_f(pack_bf16(lo_f(dh[k >> 1]) * lo_f(u[k >> 1]), 0.0f));
-          float r = ((ds * (1.0f + gv[k])) * e[k]) * k2m64;
-          u32 w = dg[k >> 1];
-          u32 rb = pack_bf16(r, r);
-          dg[k >> 1] = (k & 1) ? ((w & 0x0000ffffu) | (rb & 0xffff0000u)) : ((w & 0xffff0000u) | (rb & 0x0000ffffu));
-        }
-      }
-    }
+    eval<false>(dh, g, u, dg, du);
+    if (__builtin_expect(any_far(g), 0)) eval<true>(dh, g, u, dg, du);
   }
 };
 

@@ -78,39 +78,17 @@ mxfp8_status launch(const void *kernel, int64_t blocks, const Args &a, void *str
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
-#ifndef MX_COL_KERNEL
-#define MX_COL_KERNEL 0  // 1: register-resident strip kernel, 0: LDS-tiled kernel
-#endif
-
 // Launch of the colwise / both-layout kernel over `batches` stacked [M, N]
 // problems (batches > 1 only for the 3D cast).
 template <class Op>
 mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream) {
-#if MX_COL_KERNEL
-  const int64_t n_rt = (a.M + mx::kSM - 1) / mx::kSM, n_ct = (a.N + mx::kSC - 1) / mx::kSC;
-  if (n_rt > INT32_MAX || n_ct > INT32_MAX) return MXFP8_ERR_OVERFLOW;
-  // Split each row strip's columns into segments only when there are too
-  // few strips to fill the chip (about 2048 workgroups, 8 per CU).
-  int64_t strips;
-  if (!mul_ok(n_rt, batches, &strips)) return MXFP8_ERR_OVERFLOW;
-  int64_t n_seg = (2048 + strips - 1) / strips;
-  if (n_seg > n_ct) n_seg = n_ct;
-  if (n_seg < 1) n_seg = 1;
-  a.n_rt = (int32_t)n_rt;
-  a.n_ct = (int32_t)n_ct;
-  a.n_seg = (int32_t)n_seg;
-  int64_t blocks;
-  if (!mul_ok(strips, n_seg, &blocks)) return MXFP8_ERR_OVERFLOW;
-  const void *k = rows ? (const void *)&mx::k_strip<Op, true> : (const void *)&mx::k_strip<Op, false>;
-#else
   const int64_t n_rt = (a.M + mx::kTM - 1) / mx::kTM, n_ct = (a.N + mx::kTC - 1) / mx::kTC;
   if (n_rt > INT32_MAX || n_ct > INT32_MAX) return MXFP8_ERR_OVERFLOW;
   a.n_rt = (int32_t)n_rt;
   a.n_ct = (int32_t)n_ct;
-  int64_t blocks;
-  if (!mul_ok(n_rt, n_ct, &blocks) || !mul_ok(blocks, batches, &blocks)) return MXFP8_ERR_OVERFLOW;
+  int64_t blocks, per;
+  if (!mul_ok(n_rt, n_ct, &per) || per > UINT32_MAX || !mul_ok(per, batches, &blocks)) return MXFP8_ERR_OVERFLOW;
   const void *k = rows ? (const void *)&mx::k_tiled<Op, true> : (const void *)&mx::k_tiled<Op, false>;
-#endif
   return launch(k, blocks, a, stream);
 }
 

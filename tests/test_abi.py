@@ -163,3 +163,4 @@ def test_3d_errors():
     assert q3d(w=A + 2) == ALIGN
     assert q3d(q=A + 8) == ALIGN
     assert q3d(E=1 << 40, stride_e=1 << 30) == OVERFLOW
+
