@@ -34,6 +34,9 @@
  *  - Alignment: input pointers and E4M3 output pointers 16-byte aligned,
  *    bf16 ld_* multiples of 8 elements, E4M3 ld_* multiples of 16 bytes.
  *    Scale pointers and scale ld_* have no alignment requirement.
+ *  - Colwise and both-layout calls (and the 3D cast) need bf16 input ld_*
+ *    below 2^24 elements and output ld_* below 2^25 bytes (so M below
+ *    about 33 million rows); larger strides return MXFP8_ERR_OVERFLOW.
  *  - Outputs must not alias inputs or each other (not checked).
  *  - Calls are thread-safe; the library keeps no mutable global state.
  */

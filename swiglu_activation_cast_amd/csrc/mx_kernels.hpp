@@ -50,6 +50,14 @@ struct Args {
 
 __device__ __forceinline__ V4 load16(const uint16_t *p) { return *reinterpret_cast<const V4 *>(p); }
 
+// p + off bytes, with p wave-uniform and off a 32-bit per-lane offset: the
+// compiler then addresses through an SGPR base plus one VGPR offset
+// (global_* saddr form) instead of a 64-bit address per lane and row.
+template <class T>
+__device__ __forceinline__ T *byte_off(T *p, u32 off) {
+  return reinterpret_cast<T *>(reinterpret_cast<uintptr_t>(p) + off);
+}
+
 // Every input byte is read once and every output byte written once, so
 // both go through the nontemporal (streaming) cache policy: they do not
 // displace the scale lines that neighbouring tiles are still completing
@@ -61,25 +69,39 @@ __device__ __forceinline__ V4 load16(const uint16_t *p) { return *reinterpret_ca
 #ifndef MX_NT_STORE
 #define MX_NT_STORE 1
 #endif
+
+// All buffers live in device (global) memory.  The kernel parameters are
+// generic pointers inside a struct, so every access goes through these
+// helpers, which name the global address space explicitly: the compiler then
+// emits global_* instructions (SGPR base + 32-bit VGPR offset available,
+// counted on vmcnt only) instead of flat_* with a 64-bit address per lane.
+#define MX_GLOBAL __attribute__((address_space(1)))
+typedef u32 u32x4_t __attribute__((ext_vector_type(4)));
+
+template <class T>
+__device__ __forceinline__ MX_GLOBAL T *gptr(T *p) {
+  return (MX_GLOBAL T *)p;
+}
+
 template <class T>
 __device__ __forceinline__ void store_stream(T *p, T v) {
 #if MX_NT_STORE
-  __builtin_nontemporal_store(v, p);
+  __builtin_nontemporal_store(v, gptr(p));
 #else
-  *p = v;
+  *gptr(p) = v;
 #endif
 }
+
+__device__ __forceinline__ void store_byte(uint8_t *p, uint8_t v) { *gptr(p) = v; }
 
 __device__ __forceinline__ V4 load16_stream(const uint16_t *p) {
 #if MX_NT_LOAD
-  typedef u32 u32x4_t __attribute__((ext_vector_type(4)));
-  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
-  return V4{v.x, v.y, v.z, v.w};
+  u32x4_t v = __builtin_nontemporal_load(gptr(reinterpret_cast<const u32x4_t *>(p)));
 #else
-  return load16(p);
+  u32x4_t v = *gptr(reinterpret_cast<const u32x4_t *>(p));
 #endif
+  return V4{v.x, v.y, v.z, v.w};
 }
-
 
 // Blocks are dispatched round-robin over the 8 XCDs; renumber them so each
 // XCD works through one contiguous range of tiles (neighbouring tiles share
@@ -127,7 +149,7 @@ __global__ __launch_bounds__(256) void k_rowwise(const Args a) {
         if (c < nch) {
           const int64_t col = o * a.N + c * 8;
           store_stream(reinterpret_cast<unsigned long long *>(qr + col), ((unsigned long long)q.y << 32) | q.x);
-          if ((lane & 3) == 0) sr[col >> 5] = (uint8_t)b;
+          if ((lane & 3) == 0) store_byte(sr + (col >> 5), (uint8_t)b);
         }
       }
     }
@@ -144,7 +166,10 @@ __global__ __launch_bounds__(256) void k_rowwise(const Args a) {
 #ifndef MX_ORDER
 #define MX_ORDER 2  // 0: row tiles fastest, 1: column tiles fastest, 2: bands of row tiles
 #endif
-constexpr int kBand = 32;  // row tiles per band (tile order 2)
+#ifndef MX_BAND
+#define MX_BAND 32
+#endif
+constexpr int kBand = MX_BAND;  // row tiles per band (tile order 2)
 constexpr int kTM = MX_TM;              // tile rows (multiple of 32)
 constexpr int kTC = MX_TC;              // tile source columns
 constexpr int kRS = kTM + 8;            // LDS row stride of one transposed column (bf16)
@@ -152,10 +177,23 @@ constexpr int kCPR = kTC / 8;           // 8-column chunks per tile row
 constexpr int kRPT = kTM * kCPR / 256;  // rows per thread in the load phase
 constexpr int kG = kTM / 16;            // 16-row groups per tile column
 static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0, "tile shape");
+#ifndef MX_LDS_SEQ
+#define MX_LDS_SEQ 0  // 1: outputs pass through one LDS slot in turn
+#endif
+#ifndef MX_LOAD_SPLIT
+#define MX_LOAD_SPLIT 1  // load the thread's rows in this many fenced parts
+#endif
+constexpr int kLoadSplit = MX_LOAD_SPLIT;
+static_assert(kRPT % kLoadSplit == 0, "load split must divide the rows per thread");
+
+#ifndef MX_MIN_WAVES
+#define MX_MIN_WAVES 1
+#endif
 
 template <class Op, bool ROWS>
-__global__ __launch_bounds__(256) void k_tiled(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVES, 8))) void k_tiled(const Args a) {
+  constexpr int kLdsSlots = MX_LDS_SEQ ? 1 : Op::OUT;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsSlots][kTC][kRS];
   const int t = threadIdx.x;
   const u32 L = xcd_remap(blockIdx.x, gridDim.x);
   const u32 per = (u32)a.n_rt * (u32)a.n_ct;  // tiles per batch
@@ -178,42 +216,52 @@ __global__ __launch_bounds__(256) void k_tiled(const Args a) {
   const int64_t col = n0 + cc * 8;
   const bool colok = col < a.N;
   V4 out[kRPT][Op::OUT];
-  {
-    V4 in[kRPT][Op::IN];
+  constexpr int kPart = kRPT / kLoadSplit;  // rows loaded together
+  const int r0 = rg * kRPT;                  // first tile row of this thread
+  const u32 cl = colok ? (u32)cc * 8 : 0;    // lanes past N read column n0 (unused)
+  // Rows past M are read as row M-1 and columns past N as column n0: both
+  // stay in bounds, and their values only reach 32-row blocks or a lane's
+  // own columns that are never stored (M is a multiple of 32 here).
+  const u32 rmax = (u32)min<int64_t>(a.M - 1 - m0, kTM - 1);
 #pragma unroll
-    for (int i = 0; i < kRPT; i++) {
-      const int64_t m = m0 + rg * kRPT + i;
-      const bool ok = colok && m < a.M;
+  for (int h = 0; h < kLoadSplit; h++) {
+    V4 in[kPart][Op::IN];
 #pragma unroll
-      for (int j = 0; j < Op::IN; j++)
-        in[i][j] = ok ? load16_stream(a.in[j] + e * a.bstride_in + m * a.ld_in[j] + col) : V4{0, 0, 0, 0};
+    for (int i = 0; i < kPart; i++) {
+      const u32 r = min((u32)(r0 + h * kPart + i), rmax);
+#pragma unroll
+      for (int j = 0; j < Op::IN; j++) {
+        const uint16_t *tp = a.in[j] + e * a.bstride_in + m0 * a.ld_in[j] + n0;  // uniform
+        in[i][j] = load16_stream(byte_off(tp, (r * (u32)a.ld_in[j] + cl) * 2u));
+      }
     }
 #pragma unroll
-    for (int i = 0; i < kRPT; i++) Op::apply(in[i], out[i]);
+    for (int i = 0; i < kPart; i++) Op::apply(in[i], out[h * kPart + i]);
+    if constexpr (kLoadSplit > 1) __builtin_amdgcn_sched_barrier(0);  // bound the live loads
   }
 
   if constexpr (ROWS) {
 #pragma unroll
     for (int i = 0; i < kRPT; i++) {
-      const int64_t m = m0 + rg * kRPT + i;
 #pragma unroll
       for (int o = 0; o < Op::OUT; o++) {
         u32 am = max_xor2(max_xor1(amax_bits<4>(&out[i][o].x)));
         u32 b = e8m0_rceil(am);
         uint2 q = quant8(&out[i][o].x, b);
-        if (colok && m < a.M) {
-          const int64_t oc = o * a.N + col;
-          store_stream(reinterpret_cast<unsigned long long *>(a.q_row + m * a.ld_q_row + oc),
+        if (colok && m0 + r0 + i < a.M) {
+          const int64_t oc = o * a.N + n0;
+          uint8_t *qp = a.q_row + (m0 + i) * a.ld_q_row + oc;  // uniform
+          store_stream(reinterpret_cast<unsigned long long *>(byte_off(qp, (u32)r0 * (u32)a.ld_q_row + cl)),
                        ((unsigned long long)q.y << 32) | q.x);
-          if ((cc & 3) == 0) a.s_row[m * a.ld_s_row + (oc >> 5)] = (uint8_t)b;
+          uint8_t *sp = a.s_row + (m0 + i) * a.ld_s_row + (oc >> 5);  // uniform
+          if ((cc & 3) == 0) store_byte(byte_off(sp, (u32)r0 * (u32)a.ld_s_row + (cl >> 5)), (uint8_t)b);
         }
       }
     }
   }
 
   // ---- transpose into LDS: column (8*cc + k), rows kRPT*rg .. +kRPT-1, four at a time
-#pragma unroll
-  for (int o = 0; o < Op::OUT; o++) {
+  auto to_lds = [&](int o, int slot) {
 #pragma unroll
     for (int i0 = 0; i0 < kRPT; i0 += 4) {
 #pragma unroll
@@ -228,30 +276,47 @@ __global__ __launch_bounds__(256) void k_tiled(const Args a) {
           p01 = (r0[w] & 0xffffu) | (r1[w] << 16);
           p23 = (r2[w] & 0xffffu) | (r3[w] << 16);
         }
-        *reinterpret_cast<uint2 *>(&lds[o][cc * 8 + k][rg * kRPT + i0]) = make_uint2(p01, p23);
+        *reinterpret_cast<uint2 *>(&lds[slot][cc * 8 + k][rg * kRPT + i0]) = make_uint2(p01, p23);
       }
     }
-  }
-  __syncthreads();
+  };
 
-  // ---- colwise: item = (output o, column c, 16-row group g); lanes g, g^1 share a block
+  // ---- colwise: item = (column c, 16-row group g); lanes g, g^1 share a block
+  auto from_lds = [&](int o, int slot) {
 #pragma unroll
-  for (int p = 0; p < Op::OUT * kTC * kG / 256; p++) {
-    const int i = t + 256 * p;
-    const int g = i % kG, c = (i / kG) % kTC, o = i / (kG * kTC);
-    const V4 v0 = *reinterpret_cast<const V4 *>(&lds[o][c][16 * g]);
-    const V4 v1 = *reinterpret_cast<const V4 *>(&lds[o][c][16 * g + 8]);
-    const u32 v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    u32 am = max_xor1(amax_bits<8>(v));
-    u32 b = e8m0_rceil(am);
-    uint2 q0 = quant8(v, b), q1 = quant8(v + 4, b);
-    const int64_t n = n0 + c, mr = m0 + 16 * g;
-    if (n < a.N && mr < a.M) {
-      const int64_t orow = o * a.N + n;
-      typedef u32 u32x4_t __attribute__((ext_vector_type(4)));
-      store_stream(reinterpret_cast<u32x4_t *>(a.q_col + e * a.bstride_q + orow * a.ld_q_col + mr),
-                   u32x4_t{q0.x, q0.y, q1.x, q1.y});
-      if ((g & 1) == 0) a.s_col[e * a.bstride_s + orow * a.ld_s_col + (mr >> 5)] = (uint8_t)b;
+    for (int p = 0; p < kTC * kG / 256; p++) {
+      const int i = t + 256 * p;
+      const int g = i % kG, c = i / kG;
+      const V4 v0 = *reinterpret_cast<const V4 *>(&lds[slot][c][16 * g]);
+      const V4 v1 = *reinterpret_cast<const V4 *>(&lds[slot][c][16 * g + 8]);
+      const u32 v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      u32 am = max_xor1(amax_bits<8>(v));
+      u32 b = e8m0_rceil(am);
+      uint2 q0 = quant8(v, b), q1 = quant8(v + 4, b);
+      if (n0 + c < a.N && m0 + 16 * g < a.M) {
+        uint8_t *qp = a.q_col + e * a.bstride_q + (o * a.N + n0) * a.ld_q_col + m0;   // uniform
+        store_stream(reinterpret_cast<u32x4_t *>(byte_off(qp, (u32)c * (u32)a.ld_q_col + 16 * g)),
+                     u32x4_t{q0.x, q0.y, q1.x, q1.y});
+        uint8_t *sp = a.s_col + e * a.bstride_s + (o * a.N + n0) * a.ld_s_col + (m0 >> 5);  // uniform
+        if ((g & 1) == 0) store_byte(byte_off(sp, (u32)c * (u32)a.ld_s_col + (g >> 1)), (uint8_t)b);
+      }
+    }
+  };
+
+  if constexpr (kLdsSlots == Op::OUT) {
+#pragma unroll
+    for (int o = 0; o < Op::OUT; o++) to_lds(o, o);
+    __syncthreads();
+#pragma unroll
+    for (int o = 0; o < Op::OUT; o++) from_lds(o, o);
+  } else {
+    // one LDS slot, the outputs in turn
+#pragma unroll
+    for (int o = 0; o < Op::OUT; o++) {
+      if (o > 0) __syncthreads();  // the previous output's reads are done
+      to_lds(o, 0);
+      __syncthreads();
+      from_lds(o, 0);
     }
   }
 }

@@ -35,6 +35,19 @@ bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The colwise kernel addresses each 128x128 tile from a wave-uniform base
+// with 32-bit per-lane offsets that reach 127 row strides: keep them below
+// 2^32 bytes.
+constexpr int64_t kMaxLdIn = int64_t(1) << 24;   // bf16 elements
+constexpr int64_t kMaxLdOut = int64_t(1) << 25;  // bytes
+
+bool tile_offsets_ok(const int64_t *ld_in, int n_in, int64_t ld_q_row, int64_t ld_s_row, int64_t ld_q_col,
+                     int64_t ld_s_col) {
+  for (int j = 0; j < n_in; j++)
+    if (ld_in[j] >= kMaxLdIn) return false;
+  return ld_q_row < kMaxLdOut && ld_s_row < kMaxLdOut && ld_q_col < kMaxLdOut && ld_s_col < kMaxLdOut;
+}
+
 // Checks shared by the 2-D entry points.  W = out_mult * N is the output
 // width.  `blocked_cols` says whether the rowwise 32-blocks run along N.
 mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, int n_in, int64_t M,
@@ -66,6 +79,8 @@ mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, in
     if (!extent_ok(M, N, ld_in[j])) return MXFP8_ERR_OVERFLOW;
   if (rows && (!extent_ok(M, W, ld_q_row) || !extent_ok(M, W / 32, ld_s_row))) return MXFP8_ERR_OVERFLOW;
   if (cols && (!extent_ok(W, M, ld_q_col) || !extent_ok(W, M / 32, ld_s_col))) return MXFP8_ERR_OVERFLOW;
+  if (cols && !tile_offsets_ok(ld_in, n_in, rows ? ld_q_row : 0, rows ? ld_s_row : 0, ld_q_col, ld_s_col))
+    return MXFP8_ERR_OVERFLOW;
   return MXFP8_OK;
 }
 
@@ -175,6 +190,8 @@ mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t
   if (!mul_ok(N, ld_w, &slab)) return MXFP8_ERR_OVERFLOW;
   if (E > 1 && (stride_e < slab || stride_e % 8 != 0)) return MXFP8_ERR_STRIDE;
   if (!aligned16(w) || !aligned16(q)) return MXFP8_ERR_ALIGN;
+  const int64_t ld_one[1] = {ld_w};
+  if (!tile_offsets_ok(ld_one, 1, 0, 0, N, N / 32)) return MXFP8_ERR_OVERFLOW;
   int64_t in_ext, out_ext;
   if (!mul_ok(E - 1, stride_e, &in_ext) || !add_ok(in_ext, slab, &in_ext) || in_ext >= (INT64_MAX >> 2))
     return MXFP8_ERR_OVERFLOW;

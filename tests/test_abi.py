@@ -164,3 +164,15 @@ def test_3d_errors():
     assert q3d(q=A + 8) == ALIGN
     assert q3d(E=1 << 40, stride_e=1 << 30) == OVERFLOW
 
+
+def test_colwise_stride_limits():
+    # the colwise kernel addresses a tile with 32-bit offsets: oversized
+    # strides are refused before anything launches
+    assert q2d(layout=2, ld_x=1 << 24) == OVERFLOW
+    assert q2d(layout=2, ld_q_col=1 << 25) == OVERFLOW
+    assert fwd(layout=3, ld_q_row=1 << 25) == OVERFLOW
+    assert q3d(ld_w=1 << 24, stride_e=(1 << 24) * 64) == OVERFLOW
+    assert q3d(N=1 << 25, stride_e=(1 << 25) * 40) == OVERFLOW
+    # rowwise-only calls have no such limit (stride check fails first here)
+    assert q2d(layout=1, ld_x=(1 << 24) + 4) == STRIDE
+
