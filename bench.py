@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fused SwiGLU+MXFP8 cast achieved HBM GB/s (% of peak), fwd/bwd, both scales"
 M_ROWS, N_COLS = 131072, 8192
 WORKLOAD = "swiglu_131072x8192_w13"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_bwd_both_131072x8192.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_swiglu_131072x8192_bench.txt")
 
 
 def parse():
@@ -52,6 +52,24 @@ def kernel_source_hash() -> str:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(src_hash: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated on a device copy), or
+    None when that summary was taken with different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if not line.startswith("#") and ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_hash") != src_hash:
+        return None
+    v = fields.get(f"{kernel}_hbm_bytes_per_launch")
+    return int(v) if v is not None else None
 
 
 def time_launches(fn, iters, warmup):
@@ -216,13 +234,8 @@ def main():
     if fwd_s > bwd_s:
         dom_bytes, dom_s, dom_name = (fwd_bytes, fwd_s, "k_tiled<OpFwd, rowwise+colwise>")
     achieved = metrics.gbps(dom_bytes, dom_s)
-    traffic = None
     src_hash = kernel_source_hash()
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == src_hash:
-            traffic = tr.get("hbm_bytes_per_launch")
+    traffic = measured_traffic(src_hash, "bwd_both" if dom_bytes == bwd_bytes else "fwd_both")
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),

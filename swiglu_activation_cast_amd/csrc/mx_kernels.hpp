@@ -177,14 +177,7 @@ constexpr int kCPR = kTC / 8;           // 8-column chunks per tile row
 constexpr int kRPT = kTM * kCPR / 256;  // rows per thread in the load phase
 constexpr int kG = kTM / 16;            // 16-row groups per tile column
 static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0, "tile shape");
-#ifndef MX_LDS_SEQ
-#define MX_LDS_SEQ 0  // 1: outputs pass through one LDS slot in turn
-#endif
-#ifndef MX_LOAD_SPLIT
-#define MX_LOAD_SPLIT 1  // load the thread's rows in this many fenced parts
-#endif
-constexpr int kLoadSplit = MX_LOAD_SPLIT;
-static_assert(kRPT % kLoadSplit == 0, "load split must divide the rows per thread");
+
 
 #ifndef MX_MIN_WAVES
 #define MX_MIN_WAVES 1
@@ -192,10 +185,9 @@ static_assert(kRPT % kLoadSplit == 0, "load split must divide the rows per threa
 
 template <class Op, bool ROWS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVES, 8))) void k_tiled(const Args a) {
-  constexpr int kLdsSlots = MX_LDS_SEQ ? 1 : Op::OUT;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsSlots][kTC][kRS];
-  const int t = threadIdx.x;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
   const u32 L = xcd_remap(blockIdx.x, gridDim.x);
+  const int t = threadIdx.x;
   const u32 per = (u32)a.n_rt * (u32)a.n_ct;  // tiles per batch
   const int64_t e = L / per;
   const u32 l = L % per;
@@ -216,19 +208,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
   const int64_t col = n0 + cc * 8;
   const bool colok = col < a.N;
   V4 out[kRPT][Op::OUT];
-  constexpr int kPart = kRPT / kLoadSplit;  // rows loaded together
   const int r0 = rg * kRPT;                  // first tile row of this thread
   const u32 cl = colok ? (u32)cc * 8 : 0;    // lanes past N read column n0 (unused)
   // Rows past M are read as row M-1 and columns past N as column n0: both
   // stay in bounds, and their values only reach 32-row blocks or a lane's
   // own columns that are never stored (M is a multiple of 32 here).
   const u32 rmax = (u32)min<int64_t>(a.M - 1 - m0, kTM - 1);
+  {
+    V4 in[kRPT][Op::IN];
 #pragma unroll
-  for (int h = 0; h < kLoadSplit; h++) {
-    V4 in[kPart][Op::IN];
-#pragma unroll
-    for (int i = 0; i < kPart; i++) {
-      const u32 r = min((u32)(r0 + h * kPart + i), rmax);
+    for (int i = 0; i < kRPT; i++) {
+      const u32 r = min((u32)(r0 + i), rmax);
 #pragma unroll
       for (int j = 0; j < Op::IN; j++) {
         const uint16_t *tp = a.in[j] + e * a.bstride_in + m0 * a.ld_in[j] + n0;  // uniform
@@ -236,8 +226,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
       }
     }
 #pragma unroll
-    for (int i = 0; i < kPart; i++) Op::apply(in[i], out[h * kPart + i]);
-    if constexpr (kLoadSplit > 1) __builtin_amdgcn_sched_barrier(0);  // bound the live loads
+    for (int i = 0; i < kRPT; i++) Op::apply(in[i], out[i]);
   }
 
   if constexpr (ROWS) {
@@ -303,22 +292,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
     }
   };
 
-  if constexpr (kLdsSlots == Op::OUT) {
 #pragma unroll
-    for (int o = 0; o < Op::OUT; o++) to_lds(o, o);
-    __syncthreads();
+  for (int o = 0; o < Op::OUT; o++) to_lds(o, o);
+  __syncthreads();
 #pragma unroll
-    for (int o = 0; o < Op::OUT; o++) from_lds(o, o);
-  } else {
-    // one LDS slot, the outputs in turn
-#pragma unroll
-    for (int o = 0; o < Op::OUT; o++) {
-      if (o > 0) __syncthreads();  // the previous output's reads are done
-      to_lds(o, 0);
-      __syncthreads();
-      from_lds(o, 0);
-    }
-  }
+  for (int o = 0; o < Op::OUT; o++) from_lds(o, o);
 }
 
 }  // namespace mx
