@@ -309,6 +309,24 @@ def run_detail(inp, fwd_out, bwd_out, stream):
             res[f"{op}_{name}"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nbytes, avg), 1),
                                    "frac": round(metrics.gbps(nbytes, avg) / metrics.HBM_PEAK_GBPS, 4)}
     print("bench: per-layout timing done", file=sys.stderr, flush=True)
+    # the unfused two-kernel pipeline (bf16 activation written, then the plain
+    # cast of it), both layouts: the pages' baseline structure
+    h = torch.empty((M, N), dtype=torch.bfloat16, device=inp.gate.device)
+    y = torch.empty((M, 2 * N), dtype=torch.bfloat16, device=inp.gate.device)
+
+    def unfused_fwd():
+        mx.mxfp8_swiglu_fwd_bf16(inp.gate, inp.up, out=h, stream=stream)
+        mx.mxfp8_quant_2d(h, rowwise=True, colwise=True, out=fwd_out, stream=stream)
+
+    def unfused_bwd():
+        mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up, out=y, stream=stream)
+        mx.mxfp8_quant_2d(y, rowwise=True, colwise=True, out=bwd_out, stream=stream)
+
+    for name, fn, fused in (("unfused_fwd_both", unfused_fwd, "fwd_both"), ("unfused_bwd_both", unfused_bwd, "bwd_both")):
+        avg, _ = time_launches(fn, 10, 2)
+        res[name] = {"us": round(avg * 1e6, 2), "fused_speedup": round(avg * 1e6 / res[fused]["us"], 3)}
+    del h, y
+    torch.cuda.empty_cache()
     # plain 2D cast of the gate half (colwise, the "dim1" cast) and rowwise
     for lay, name in ((mx.ROWWISE, "row"), (mx.COLWISE, "col")):
         fl = dict(rowwise=bool(lay & 1), colwise=bool(lay & 2))

@@ -128,6 +128,25 @@ mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t
                                     int64_t stride_e, int64_t ld_w,
                                     void *q, void *s, void *stream);
 
+/*
+ * The activation alone, written as bf16 instead of being cast: the first
+ * kernel of the unfused two-kernel pipeline (activation, then
+ * mxfp8_quant_2d) that the fused calls replace.  "Add swiglu + MXFP8 fused
+ * CuTe DSL kernel", Performance: the baseline arm is a fused activation
+ * kernel followed by the standalone quantizer.  The values are the ones the
+ * fused calls quantize, so mxfp8_quant_2d of this output equals the fused
+ * result bit for bit.
+ *   gate, up, dh : bf16 [M, N] as in the fused calls; N % 8 == 0.
+ *   h            : bf16 [M, N], row stride ld_h (multiple of 8, >= N).
+ *   dgdu         : bf16 [M, 2N] = [dGate | dUp], row stride ld_dgdu (>= 2N).
+ * Same pointer, alignment and status conventions as above.
+ */
+mxfp8_status mxfp8_swiglu_fwd_bf16(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up,
+                                   int64_t M, int64_t N, void *h, int64_t ld_h, void *stream);
+mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate,
+                                   const void *up, int64_t ld_up, int64_t M, int64_t N,
+                                   void *dgdu, int64_t ld_dgdu, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *mxfp8_status_str(mxfp8_status status);
 

@@ -17,7 +17,9 @@ from ._binding import (
     mxfp8_quant_2d,
     mxfp8_quant_3d_colwise,
     mxfp8_swiglu_bwd,
+    mxfp8_swiglu_bwd_bf16,
     mxfp8_swiglu_fwd,
+    mxfp8_swiglu_fwd_bf16,
     status_str,
 )
 
@@ -33,6 +35,8 @@ __all__ = [
     "mxfp8_quant_2d",
     "mxfp8_quant_3d_colwise",
     "mxfp8_swiglu_bwd",
+    "mxfp8_swiglu_bwd_bf16",
     "mxfp8_swiglu_fwd",
+    "mxfp8_swiglu_fwd_bf16",
     "status_str",
 ]

@@ -39,6 +39,8 @@ _SIGNATURES = {
     "mxfp8_swiglu_bwd": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
     "mxfp8_quant_2d": [_p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
     "mxfp8_quant_3d_colwise": [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p],
+    "mxfp8_swiglu_fwd_bf16": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
+    "mxfp8_swiglu_bwd_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
 }
 
 _lib = None
@@ -197,6 +199,44 @@ def mxfp8_quant_3d_colwise(w: torch.Tensor, *, out: Optional[Sequence[torch.Tens
                                       _stream(w.device, stream))
     _check("mxfp8_quant_3d_colwise", st)
     return q, s
+
+
+def _bf16_out(t, M, W, device):
+    if t is None:
+        return torch.empty((M, W), dtype=torch.bfloat16, device=device)
+    if t.dtype != torch.bfloat16 or tuple(t.shape) != (M, W) or (W > 1 and t.stride(1) != 1):
+        raise ValueError(f"output must be a bf16 [{M}, {W}] tensor with unit column stride")
+    return t
+
+
+def mxfp8_swiglu_fwd_bf16(gate: torch.Tensor, up: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None):
+    """h = bf16(bf16(silu(gate)) * up) written as bf16 (the unfused pipeline's activation)."""
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if gate.shape != up.shape or gate.device != up.device:
+        raise ValueError("gate and up must have the same shape and device")
+    M, N = gate.shape
+    h = _bf16_out(out, M, N, gate.device)
+    st = lib().mxfp8_swiglu_fwd_bf16(pg, ldg, pu, ldu, M, N, h.data_ptr(), h.stride(0) if M > 1 else max(N, 8),
+                                     _stream(gate.device, stream))
+    _check("mxfp8_swiglu_fwd_bf16", st)
+    return h
+
+
+def mxfp8_swiglu_bwd_bf16(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, *,
+                          out: Optional[torch.Tensor] = None, stream=None):
+    """[dgate | dup] of silu(gate) * up for upstream dh, written as bf16 [M, 2N]."""
+    pd, ldd = _bf16_matrix(dh, "dh")
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if not (dh.shape == gate.shape == up.shape) or not (dh.device == gate.device == up.device):
+        raise ValueError("dh, gate and up must have the same shape and device")
+    M, N = gate.shape
+    y = _bf16_out(out, M, 2 * N, gate.device)
+    st = lib().mxfp8_swiglu_bwd_bf16(pd, ldd, pg, ldg, pu, ldu, M, N, y.data_ptr(),
+                                     y.stride(0) if M > 1 else max(2 * N, 8), _stream(gate.device, stream))
+    _check("mxfp8_swiglu_bwd_bf16", st)
+    return y
 
 
 def gated_act_mxfp8_forward(gated_input: torch.Tensor, *, rowwise: bool = True, colwise: bool = False, out=None,

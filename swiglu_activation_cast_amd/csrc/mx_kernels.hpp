@@ -156,6 +156,46 @@ __global__ __launch_bounds__(256) void k_rowwise(const Args a) {
   }
 }
 
+// ------------------------------------------------------------------- values
+// The activation alone, in bf16: h (forward) or [dgate | dup] (backward) is
+// written to memory instead of being cast.  Together with the plain 2D cast
+// this is the unfused two-kernel pipeline the fused kernels replace ("Add
+// swiglu + MXFP8 fused CuTe DSL kernel", Performance: the baseline arm is a
+// fused activation kernel followed by the standalone quantizer).  It runs
+// the same value code as the fused kernels, so quantizing its output gives
+// the fused kernels' result bit for bit.  One wavefront per row, 8 columns
+// per lane, as k_rowwise.
+template <class Op, int U>
+__global__ __launch_bounds__(256) void k_values(const Args a, uint16_t *dst, int64_t ld_dst) {
+  const int lane = threadIdx.x & 63;
+  const int64_t m = (int64_t)blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (m >= a.M) return;  // wave-uniform
+  const int64_t nch = a.N >> 3;
+  const uint16_t *row[Op::IN];
+#pragma unroll
+  for (int j = 0; j < Op::IN; j++) row[j] = a.in[j] + m * a.ld_in[j];
+  uint16_t *dr = dst + m * ld_dst;
+  for (int64_t c0 = 0; c0 < nch; c0 += 64 * U) {
+    V4 in[U][Op::IN];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t c = c0 + 64 * u + lane;
+#pragma unroll
+      for (int j = 0; j < Op::IN; j++) in[u][j] = (c < nch) ? load16_stream(row[j] + c * 8) : V4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int64_t c = c0 + 64 * u + lane;
+      V4 out[Op::OUT];
+      Op::apply(in[u], out);
+      if (c < nch)
+#pragma unroll
+        for (int o = 0; o < Op::OUT; o++)
+          store_stream(reinterpret_cast<u32x4_t *>(dr + o * a.N + c * 8), u32x4_t{out[o].x, out[o].y, out[o].z, out[o].w});
+    }
+  }
+}
+
 // -------------------------------------------------------------------- tiled
 #ifndef MX_TM
 #define MX_TM 128

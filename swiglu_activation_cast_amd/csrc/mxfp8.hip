@@ -107,6 +107,39 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream) {
   return launch(k, blocks, a, stream);
 }
 
+// Checks of the bf16 value entry points: inputs as for the fused calls,
+// one bf16 output [M, W] with row stride ld_out.
+mxfp8_status check_values(const void *const *in, const int64_t *ld_in, int n_in, int64_t M, int64_t N,
+                          const void *out, int64_t ld_out, int64_t W) {
+  if (M < 0 || N < 0 || N % 8 != 0) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  for (int j = 0; j < n_in; j++)
+    if (!in[j]) return MXFP8_ERR_NULL;
+  if (!out) return MXFP8_ERR_NULL;
+  for (int j = 0; j < n_in; j++)
+    if (ld_in[j] < N || ld_in[j] % 8 != 0) return MXFP8_ERR_STRIDE;
+  if (ld_out < W || ld_out % 8 != 0) return MXFP8_ERR_STRIDE;
+  for (int j = 0; j < n_in; j++)
+    if (!aligned16(in[j])) return MXFP8_ERR_ALIGN;
+  if (!aligned16(out)) return MXFP8_ERR_ALIGN;
+  for (int j = 0; j < n_in; j++)
+    if (!extent_ok(M, N, ld_in[j])) return MXFP8_ERR_OVERFLOW;
+  if (!extent_ok(M, W, ld_out)) return MXFP8_ERR_OVERFLOW;
+  return MXFP8_OK;
+}
+
+template <class Op>
+mxfp8_status launch_values(const Args &a, void *dst, int64_t ld_dst, void *stream) {
+  const int64_t blocks = (a.M + mx::kRowWaves - 1) / mx::kRowWaves;
+  if (blocks <= 0 || blocks > (int64_t)INT32_MAX / 256) return MXFP8_ERR_OVERFLOW;
+  Args copy = a;
+  uint16_t *d = static_cast<uint16_t *>(dst);
+  void *kargs[] = {&copy, &d, &ld_dst};
+  hipError_t err = hipLaunchKernel((const void *)&mx::k_values<Op, kRowUnroll>, dim3((unsigned)blocks), dim3(256),
+                                   kargs, 0, (hipStream_t)stream);
+  return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
 template <class Op>
 mxfp8_status dispatch_2d(const Args &a, int layout, void *stream) {
   if (layout == MXFP8_ROWWISE) {
@@ -206,6 +239,27 @@ mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t
   a.bstride_q = K * N;
   a.bstride_s = K * (N / 32);
   return launch_colwise<mx::OpQuant>(a, false, E, stream);
+}
+
+mxfp8_status mxfp8_swiglu_fwd_bf16(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
+                                   int64_t N, void *h, int64_t ld_h, void *stream) {
+  const void *in[2] = {gate, up};
+  const int64_t ld[2] = {ld_gate, ld_up};
+  mxfp8_status st = check_values(in, ld, 2, M, N, h, ld_h, N);
+  if (st != MXFP8_OK || M == 0 || N == 0) return st;
+  Args a = make_args(in, ld, 2, M, N, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
+  return launch_values<mx::OpFwd>(a, h, ld_h, stream);
+}
+
+mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate, const void *up,
+                                   int64_t ld_up, int64_t M, int64_t N, void *dgdu, int64_t ld_dgdu,
+                                   void *stream) {
+  const void *in[3] = {dh, gate, up};
+  const int64_t ld[3] = {ld_dh, ld_gate, ld_up};
+  mxfp8_status st = check_values(in, ld, 3, M, N, dgdu, ld_dgdu, 2 * N);
+  if (st != MXFP8_OK || M == 0 || N == 0) return st;
+  Args a = make_args(in, ld, 3, M, N, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
+  return launch_values<mx::OpBwd>(a, dgdu, ld_dgdu, stream);
 }
 
 const char *mxfp8_status_str(mxfp8_status status) {

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     lib = mx.lib()
     names = declared_functions()
     assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_quant_2d", "mxfp8_quant_3d_colwise",
-                     "mxfp8_status_str"}
+                     "mxfp8_swiglu_fwd_bf16", "mxfp8_swiglu_bwd_bf16", "mxfp8_status_str"}
     for n in names:
         assert getattr(lib, n) is not None
 
@@ -175,4 +175,22 @@ def test_colwise_stride_limits():
     assert q3d(N=1 << 25, stride_e=(1 << 25) * 40) == OVERFLOW
     # rowwise-only calls have no such limit (stride check fails first here)
     assert q2d(layout=1, ld_x=(1 << 24) + 4) == STRIDE
+
+
+def test_bf16_value_entry_points_errors():
+    lib = mx.lib()
+    f = lib.mxfp8_swiglu_fwd_bf16
+    b = lib.mxfp8_swiglu_bwd_bf16
+    assert f(A, 128, A, 128, 64, 128, None, 128, None) == NULL
+    assert f(None, 128, A, 128, 64, 128, A, 128, None) == NULL
+    assert f(A, 128, A, 128, 64, 12, A, 128, None) == SHAPE        # N % 8 != 0
+    assert f(A, 128, A, 128, -1, 128, A, 128, None) == SHAPE
+    assert f(A, 128, A, 128, 64, 128, A, 120, None) == STRIDE      # ld_h < N
+    assert f(A, 100, A, 128, 64, 96, A, 128, None) == STRIDE       # ld not a multiple of 8
+    assert f(A + 2, 128, A, 128, 64, 128, A, 128, None) == ALIGN
+    assert f(A, 128, A, 128, 64, 128, A + 8, 128, None) == ALIGN
+    assert f(None, 128, None, 128, 0, 128, None, 128, None) == OK  # empty
+    assert b(A, 128, A, 128, A, 128, 64, 128, A, 128, None) == STRIDE   # [dg|du] needs ld >= 2N
+    assert b(A, 128, A, 128, None, 128, 64, 128, A, 256, None) == NULL
+    assert b(A, 128, A, 128, A, 128, 64, 128, A + 4, 256, None) == ALIGN
 

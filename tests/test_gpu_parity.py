@@ -406,3 +406,52 @@ def test_empty_inputs_are_noops():
     assert outs[0].shape == (0, 64) and outs[1].shape == (64, 0)
     q, s = mx.mxfp8_quant_3d_colwise(torch.zeros((0, 32, 8), dtype=torch.bfloat16, device=dev))
     assert q.numel() == 0 and s.numel() == 0
+
+
+# -------------------------------------------------- unfused pipeline (bf16)
+@pytest.mark.parametrize("M,N", [(128, 128), (96, 1056), (4096, 2048)])
+def test_bf16_values_match_oracle_and_feed_the_plain_cast(oracle_mod, M, N):
+    """The activation-only kernels agree with the oracle's values on nearly
+    all elements, and the plain 2D cast of their output equals the fused
+    cast bit for bit (same value code on the GPU).
+
+    Bound: the fp32 silu may round to the bf16 neighbour of the exact s; a
+    one-step change of s is 2^-8..2^-7 relative, which is up to two steps of
+    h = bf16(s * u) (and of du = bf16(dh * s)) when s's mantissa is near 1
+    and the product's near 2.  dg rounds one fp32 expression of exact bf16
+    operands: at most one step.  (Two bf16 steps stay below one E4M3 step,
+    which is what the fused casts are held to.)"""
+    dev = _dev()
+    print(f"case: bf16 values M={M} N={N}", flush=True)
+    inp = synth.swiglu_inputs(M, N, seed=M + 3 * N, std=2.0, outlier_rate=1e-3, device=dev)
+    h = mx.mxfp8_swiglu_fwd_bf16(inp.gate, inp.up)
+    y = mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up)
+    g, u, dh = (torch_bf16_to_bits(t) for t in (inp.gate, inp.up, inp.dh))
+    h_o = oracle_mod.swiglu_fwd_values(g, u)
+    dg_o, du_o = oracle_mod.swiglu_bwd_values(dh, g, u)
+    y_o = np.concatenate([dg_o, du_o], axis=1)
+    yb = torch_bf16_to_bits(y)
+    for name, got, want, bound in (("h", torch_bf16_to_bits(h), h_o, 2), ("dg", yb[:, :N], y_o[:, :N], 1),
+                                   ("du", yb[:, N:], y_o[:, N:], 2)):
+        steps = np.abs(got.astype(np.int32) - want.astype(np.int32))
+        zero = ((got & 0x7FFF) == 0) & ((want & 0x7FFF) == 0)
+        steps[zero] = 0  # +0 and -0
+        assert steps.max() <= bound, (name, int(steps.max()))
+        assert (steps > 0).mean() < 2e-3, name
+    for fused, vals in ((mx.mxfp8_swiglu_fwd(inp.gate, inp.up, rowwise=True, colwise=True), h),
+                        (mx.mxfp8_swiglu_bwd(inp.dh, inp.gate, inp.up, rowwise=True, colwise=True), y)):
+        plain = mx.mxfp8_quant_2d(vals, rowwise=True, colwise=True)
+        for a, b in zip(fused, plain):
+            assert torch.equal(a, b)
+
+
+def test_bf16_values_strided_output():
+    dev = _dev()
+    inp = synth.swiglu_inputs(64, 256, seed=77, device=dev, packed=True)
+    big = torch.full((64, 600), 7.0, dtype=torch.bfloat16, device=dev)
+    out = big[:, 8:520]
+    y = mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up, out=out)
+    ref = mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up)
+    assert torch.equal(y, ref)
+    assert (big[:, :8] == 7.0).all() and (big[:, 520:] == 7.0).all()
+
