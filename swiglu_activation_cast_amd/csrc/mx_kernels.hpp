@@ -16,11 +16,13 @@
 //             consecutive rows of one column (two 16-byte LDS reads), pairs
 //             with its neighbour lane for the 32-row block amax, and stores
 //             16 E4M3 bytes; eight lanes cover the tile's 128 rows of one
-//             output row, a full 128-byte line.  Tiles run in bands of 32
-//             row tiles (row tiles fastest inside a band), so each 128-byte
-//             line of either scale matrix is completed by tiles that run
-//             close together on one XCD.  The same kernel, with a batch
-//             index, is the 3D per-expert colwise cast.
+//             output row, a full 128-byte line.  Tiles run in bands of
+//             row tiles (row tiles fastest inside a band; the host picks the
+//             band width per launch), and each XCD works through one
+//             contiguous range of tiles, so each 128-byte line of either
+//             scale matrix is completed by tiles that run close together on
+//             one XCD.  The same kernel, with a batch index, is the 3D
+//             per-expert colwise cast.
 //
 // Layout facts: "Add swiglu + MXFP8 fused CuTe DSL kernel" (Summary: 1x32,
 // 32x1 or both from a single pass); "[mxfp8 moe training] update 3d quant
@@ -46,6 +48,7 @@ struct Args {
   int64_t ld_s_col;
   int64_t bstride_in, bstride_q, bstride_s;  // per-batch offsets (3D cast)
   int32_t n_rt, n_ct;                        // row tiles, column tiles
+  int32_t band;                              // row tiles per band (tile order)
 };
 
 __device__ __forceinline__ V4 load16(const uint16_t *p) { return *reinterpret_cast<const V4 *>(p); }
@@ -203,20 +206,17 @@ __global__ __launch_bounds__(256) void k_values(const Args a, uint16_t *dst, int
 #ifndef MX_TC
 #define MX_TC 128
 #endif
-#ifndef MX_ORDER
-#define MX_ORDER 2  // 0: row tiles fastest, 1: column tiles fastest, 2: bands of row tiles
+#ifndef MX_NT
+#define MX_NT 256
 #endif
-#ifndef MX_BAND
-#define MX_BAND 32
-#endif
-constexpr int kBand = MX_BAND;  // row tiles per band (tile order 2)
 constexpr int kTM = MX_TM;              // tile rows (multiple of 32)
 constexpr int kTC = MX_TC;              // tile source columns
+constexpr int kNT = MX_NT;              // threads per workgroup
 constexpr int kRS = kTM + 8;            // LDS row stride of one transposed column (bf16)
 constexpr int kCPR = kTC / 8;           // 8-column chunks per tile row
-constexpr int kRPT = kTM * kCPR / 256;  // rows per thread in the load phase
+constexpr int kRPT = kTM * kCPR / kNT;  // rows per thread in the load phase
 constexpr int kG = kTM / 16;            // 16-row groups per tile column
-static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0, "tile shape");
+static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0 && (kTC * kG) % kNT == 0, "tile shape");
 
 
 #ifndef MX_MIN_WAVES
@@ -224,23 +224,18 @@ static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0, "tile shape");
 #endif
 
 template <class Op, bool ROWS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVES, 8))) void k_tiled(const Args a) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVES, 8))) void k_tiled(const Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
   const u32 L = xcd_remap(blockIdx.x, gridDim.x);
   const int t = threadIdx.x;
   const u32 per = (u32)a.n_rt * (u32)a.n_ct;  // tiles per batch
   const int64_t e = L / per;
   const u32 l = L % per;
-#if MX_ORDER == 0  // row tiles fastest
-  const u32 rt = l % (u32)a.n_rt, ct = l / (u32)a.n_rt;
-#elif MX_ORDER == 1  // column tiles fastest
-  const u32 ct = l % (u32)a.n_ct, rt = l / (u32)a.n_ct;
-#else  // bands of kBand row tiles, row tiles fastest inside a band
-  const u32 band_tiles = (u32)kBand * (u32)a.n_ct;
+  // bands of a.band row tiles, row tiles fastest inside a band
+  const u32 band_tiles = (u32)a.band * (u32)a.n_ct;
   const u32 band = l / band_tiles, in_band = l % band_tiles;
-  const u32 rows_in_band = min((u32)kBand, (u32)a.n_rt - band * (u32)kBand);
-  const u32 rt = band * (u32)kBand + in_band % rows_in_band, ct = in_band / rows_in_band;
-#endif
+  const u32 rows_in_band = min((u32)a.band, (u32)a.n_rt - band * (u32)a.band);
+  const u32 rt = band * (u32)a.band + in_band % rows_in_band, ct = in_band / rows_in_band;
   const int64_t m0 = (int64_t)rt * kTM, n0 = (int64_t)ct * kTC;
 
   // ---- load + compute: thread owns rows m0 + kRPT*rg + i, columns col..col+7
@@ -313,8 +308,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
   // ---- colwise: item = (column c, 16-row group g); lanes g, g^1 share a block
   auto from_lds = [&](int o, int slot) {
 #pragma unroll
-    for (int p = 0; p < kTC * kG / 256; p++) {
-      const int i = t + 256 * p;
+    for (int p = 0; p < kTC * kG / kNT; p++) {
+      const int i = t + kNT * p;
       const int g = i % kG, c = i / kG;
       const V4 v0 = *reinterpret_cast<const V4 *>(&lds[slot][c][16 * g]);
       const V4 v1 = *reinterpret_cast<const V4 *>(&lds[slot][c][16 * g + 8]);

@@ -8,6 +8,7 @@
 // outputs) and Numerics and tests (launcher guards on sizes and pointer
 // alignment, each error path reachable without a device).
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <limits.h>
 #include <stdint.h>
 
@@ -35,11 +36,26 @@ bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// The colwise kernel addresses each 128x128 tile from a wave-uniform base
-// with 32-bit per-lane offsets that reach 127 row strides: keep them below
+// The colwise kernel addresses each tile from a wave-uniform base with
+// 32-bit per-lane offsets that reach (tile rows - 1) input / q_row / s_row
+// strides and (tile columns - 1) q_col / s_col strides: keep them below
 // 2^32 bytes.
-constexpr int64_t kMaxLdIn = int64_t(1) << 24;   // bf16 elements
-constexpr int64_t kMaxLdOut = int64_t(1) << 25;  // bytes
+constexpr int64_t kMaxLdIn = (int64_t(1) << 31) / mx::kTM;                                   // bf16 elements
+constexpr int64_t kMaxLdOut = (int64_t(1) << 32) / (mx::kTM > mx::kTC ? mx::kTM : mx::kTC);  // bytes
+
+// Tile order of the colwise kernel: bands of row tiles, row tiles fastest
+// inside a band.  A colwise-only launch runs bands of 128 row tiles, so the
+// tiles in flight extend each q_col output row in long contiguous runs; a
+// both-layout launch also writes rowwise lines, which favour more column
+// tiles in flight, and runs best with bands of 32 (both measured at
+// 131072 x 8192 on MI355X).
+#ifndef MX_BAND_COL
+#define MX_BAND_COL 128
+#endif
+#ifndef MX_BAND_BOTH
+#define MX_BAND_BOTH 32
+#endif
+constexpr int32_t kBandCol = MX_BAND_COL, kBandBoth = MX_BAND_BOTH;
 
 bool tile_offsets_ok(const int64_t *ld_in, int n_in, int64_t ld_q_row, int64_t ld_s_row, int64_t ld_q_col,
                      int64_t ld_s_col) {
@@ -84,12 +100,12 @@ mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, in
   return MXFP8_OK;
 }
 
-mxfp8_status launch(const void *kernel, int64_t blocks, const Args &a, void *stream) {
+mxfp8_status launch(const void *kernel, int64_t blocks, int threads, const Args &a, void *stream) {
   // Grid x is limited to 2^32 - 1 work-items; keep well inside it.
-  if (blocks <= 0 || blocks > (int64_t)INT32_MAX / 256) return MXFP8_ERR_OVERFLOW;
+  if (blocks <= 0 || blocks > (int64_t)INT32_MAX / threads) return MXFP8_ERR_OVERFLOW;
   Args copy = a;
   void *kargs[] = {&copy};
-  hipError_t err = hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(256), kargs, 0, (hipStream_t)stream);
+  hipError_t err = hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), kargs, 0, (hipStream_t)stream);
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
@@ -104,7 +120,9 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream) {
   int64_t blocks, per;
   if (!mul_ok(n_rt, n_ct, &per) || per > UINT32_MAX || !mul_ok(per, batches, &blocks)) return MXFP8_ERR_OVERFLOW;
   const void *k = rows ? (const void *)&mx::k_tiled<Op, true> : (const void *)&mx::k_tiled<Op, false>;
-  return launch(k, blocks, a, stream);
+  // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
+  a.band = (int32_t)std::min<int64_t>(rows ? kBandBoth : kBandCol, n_rt);
+  return launch(k, blocks, mx::kNT, a, stream);
 }
 
 // Checks of the bf16 value entry points: inputs as for the fused calls,
@@ -144,7 +162,7 @@ template <class Op>
 mxfp8_status dispatch_2d(const Args &a, int layout, void *stream) {
   if (layout == MXFP8_ROWWISE) {
     const int64_t blocks = (a.M + mx::kRowWaves - 1) / mx::kRowWaves;
-    return launch((const void *)&mx::k_rowwise<Op, kRowUnroll>, blocks, a, stream);
+    return launch((const void *)&mx::k_rowwise<Op, kRowUnroll>, blocks, 256, a, stream);
   }
   return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream);
 }
