@@ -18,7 +18,6 @@ expert cast, a copy-kernel ceiling).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -46,12 +45,9 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "swiglu_activation_cast_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
-    return h.hexdigest()[:16]
+    from swiglu_activation_cast_amd._build import kernel_source_hash as h
+
+    return h()
 
 
 def measured_traffic(src_hash: str, kernel: str):

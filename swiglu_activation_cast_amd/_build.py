@@ -1,6 +1,7 @@
 """Compiles the gfx950 HIP library (libmxfp8.so) in-tree with hipcc."""
 from __future__ import annotations
 
+import hashlib
 import os
 import shutil
 import subprocess
@@ -12,6 +13,16 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmxfp8.so")
 SOURCES = [os.path.join(CSRC, "mxfp8.hip")]
 ARCH = "gfx950"
+
+
+def kernel_source_hash() -> str:
+    """Short hash of the kernel sources (every file under csrc/): ties a
+    recorded profile to the code it measured."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
 
 
 def hipcc() -> str:
