@@ -1,4 +1,5 @@
-"""CPU oracle for the fused SwiGLU + MXFP8 cast -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the fused SwiGLU (and gated-activation) + MXFP8 cast --
+TEST INFRASTRUCTURE ONLY.
 
 A plain, slow, single-threaded definition (``mxfp8_oracle.c``, IEEE double)
 of what the GPU path computes.  Only the test suite, the smoke check and the
@@ -23,6 +24,10 @@ import numpy as np
 ROWWISE = 1
 COLWISE = 2
 BOTH = 3
+
+# gate activations of the gated family: act(g) * up
+SILU, GELU_TANH, GELU, RELU = 0, 1, 2, 3
+ACTS = {"silu": SILU, "gelu_tanh": GELU_TANH, "gelu": GELU, "relu": RELU}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmxfp8_oracle.so")
@@ -51,6 +56,13 @@ def _load():
         "orc_block_scale": (ctypes.c_uint8, [_p, _i64, _i64]),
         "orc_quant_block_at": (None, [_p, _i64, _i64, ctypes.c_uint8, _p, _i64]),
         "orc_quant_block": (None, [_p, _i64, _i64, _p, _i64, _p]),
+        "orc_act": (ctypes.c_double, [ctypes.c_int, ctypes.c_double]),
+        "orc_act_grad": (ctypes.c_double, [ctypes.c_int, ctypes.c_double]),
+        "orc_gated_fwd_values": (ctypes.c_int, [ctypes.c_int, _p, _p, _i64, _p]),
+        "orc_gated_bwd_values": (ctypes.c_int, [ctypes.c_int, _p, _p, _p, _i64, _p, _p]),
+        "orc_gated_fwd": (ctypes.c_int, [ctypes.c_int, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int] + [_p, _i64] * 4),
+        "orc_gated_bwd": (ctypes.c_int, [ctypes.c_int, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int]
+                          + [_p, _i64] * 4),
         "orc_swiglu_fwd_values": (None, [_p, _p, _i64, _p]),
         "orc_swiglu_bwd_values": (None, [_p, _p, _p, _i64, _p, _p]),
         "orc_quant_2d": (ctypes.c_int, [_p, _i64, _i64, _i64, ctypes.c_int] + [_p, _i64] * 4),
@@ -103,6 +115,16 @@ def silu(x: float) -> float:
     return _load().orc_silu(float(x))
 
 
+def act(a: int, x: float) -> float:
+    """The gate activation `a` (SILU, GELU_TANH, GELU, RELU) at x, in double."""
+    return _load().orc_act(int(a), float(x))
+
+
+def act_grad(a: int, x: float) -> float:
+    """Its derivative at x, in double."""
+    return _load().orc_act_grad(int(a), float(x))
+
+
 # ------------------------------------------------------------------ blocks
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
@@ -136,26 +158,37 @@ def _u16(a) -> np.ndarray:
     return a
 
 
-def swiglu_fwd_values(g, u) -> np.ndarray:
-    """h = bf16(bf16(silu(g)) * u), elementwise, as uint16 bits."""
+def gated_fwd_values(g, u, act: int = SILU) -> np.ndarray:
+    """h = bf16(bf16(act(g)) * u), elementwise, as uint16 bits."""
     g = np.ascontiguousarray(_u16(g))
     u = np.ascontiguousarray(_u16(u))
     assert g.shape == u.shape
     h = np.empty_like(g)
-    _load().orc_swiglu_fwd_values(_ptr(g), _ptr(u), g.size, _ptr(h))
+    _check(_load().orc_gated_fwd_values(int(act), _ptr(g), _ptr(u), g.size, _ptr(h)), "gated_fwd_values")
     return h
 
 
-def swiglu_bwd_values(dh, g, u):
-    """(dg, du) of h = silu(g) * u for upstream gradient dh, as uint16 bits."""
+def gated_bwd_values(dh, g, u, act: int = SILU):
+    """(dg, du) of h = act(g) * u for upstream gradient dh, as uint16 bits."""
     dh = np.ascontiguousarray(_u16(dh))
     g = np.ascontiguousarray(_u16(g))
     u = np.ascontiguousarray(_u16(u))
     assert dh.shape == g.shape == u.shape
     dg = np.empty_like(g)
     du = np.empty_like(g)
-    _load().orc_swiglu_bwd_values(_ptr(dh), _ptr(g), _ptr(u), g.size, _ptr(dg), _ptr(du))
+    _check(_load().orc_gated_bwd_values(int(act), _ptr(dh), _ptr(g), _ptr(u), g.size, _ptr(dg), _ptr(du)),
+           "gated_bwd_values")
     return dg, du
+
+
+def swiglu_fwd_values(g, u) -> np.ndarray:
+    """h = bf16(bf16(silu(g)) * u), elementwise, as uint16 bits."""
+    return gated_fwd_values(g, u, SILU)
+
+
+def swiglu_bwd_values(dh, g, u):
+    """(dg, du) of h = silu(g) * u for upstream gradient dh, as uint16 bits."""
+    return gated_bwd_values(dh, g, u, SILU)
 
 
 # ------------------------------------------------------------------ matrices
@@ -198,18 +231,19 @@ def quant_2d(x, layout: int = ROWWISE):
     return outs
 
 
-def swiglu_fwd(gate, up, layout: int = ROWWISE):
-    """Fused forward: MXFP8 cast of h = silu(gate) * up; returns (q_row, s_row, q_col, s_col)."""
+def gated_fwd(gate, up, layout: int = ROWWISE, act: int = SILU):
+    """Fused forward: MXFP8 cast of h = act(gate) * up; returns (q_row, s_row, q_col, s_col)."""
     g, ldg = _mat(gate)
     u, ldu = _mat(up)
     assert g.shape == u.shape
     M, N = g.shape
     outs = _outputs(M, N, layout)
-    _check(_load().orc_swiglu_fwd(_ptr(g), ldg, _ptr(u), ldu, M, N, layout, *_out_args(*outs)), "swiglu_fwd")
+    _check(_load().orc_gated_fwd(int(act), _ptr(g), ldg, _ptr(u), ldu, M, N, layout, *_out_args(*outs)),
+           "gated_fwd")
     return outs
 
 
-def swiglu_bwd(dh, gate, up, layout: int = ROWWISE):
+def gated_bwd(dh, gate, up, layout: int = ROWWISE, act: int = SILU):
     """Fused backward: MXFP8 cast of [dg | du]; returns (q_row, s_row, q_col, s_col), width 2N."""
     d, ldd = _mat(dh)
     g, ldg = _mat(gate)
@@ -218,10 +252,20 @@ def swiglu_bwd(dh, gate, up, layout: int = ROWWISE):
     M, N = g.shape
     outs = _outputs(M, 2 * N, layout)
     _check(
-        _load().orc_swiglu_bwd(_ptr(d), ldd, _ptr(g), ldg, _ptr(u), ldu, M, N, layout, *_out_args(*outs)),
-        "swiglu_bwd",
+        _load().orc_gated_bwd(int(act), _ptr(d), ldd, _ptr(g), ldg, _ptr(u), ldu, M, N, layout, *_out_args(*outs)),
+        "gated_bwd",
     )
     return outs
+
+
+def swiglu_fwd(gate, up, layout: int = ROWWISE):
+    """Fused forward: MXFP8 cast of h = silu(gate) * up; returns (q_row, s_row, q_col, s_col)."""
+    return gated_fwd(gate, up, layout, SILU)
+
+
+def swiglu_bwd(dh, gate, up, layout: int = ROWWISE):
+    """Fused backward: MXFP8 cast of [dg | du]; returns (q_row, s_row, q_col, s_col), width 2N."""
+    return gated_bwd(dh, gate, up, layout, SILU)
 
 
 def quant_3d_colwise(w):

@@ -40,6 +40,12 @@
  *    Colwise data is [W, M] row-major (the transpose of the [M, W] view).
  *  - 3D: blocks of 32 along N; expert e's data at q[e][k][n], scales at
  *    s[e][k][n/32].
+ *  - More gated activations.  [P1] API makes the activation a compile-time
+ *    policy, and [P1] Follow-ups plans more than SiLU without naming them.
+ *    Taken here: GELU in its exact form x * Phi(x) and in the tanh form, and
+ *    ReLU, each in place of silu with the same rounding sites:
+ *    a = bf16(act(g)), h = bf16(a * u); du = bf16(dh * a),
+ *    da = bf16(dh * u), dg = bf16(da * act'(g)).
  *
  * All real arithmetic here is IEEE double: a product of two bf16 values is
  * exact in double, and silu/sigmoid carry ~1e-16 relative error before the
@@ -214,35 +220,100 @@ double orc_silu(double x)
     return x * orc_sigmoid(x); /* -Inf * 0 = NaN, +Inf * 1 = +Inf */
 }
 
-/* Forward value of one element as eager bf16 computes it: two roundings. */
-static uint16_t fwd_value(uint16_t g, uint16_t u)
+/* Gate activations of the gated family (see the readings above). */
+enum { ORC_ACT_SILU = 0, ORC_ACT_GELU_TANH = 1, ORC_ACT_GELU = 2, ORC_ACT_RELU = 3 };
+
+#define ORC_PI 3.14159265358979323846
+
+/* Standard normal cdf and density. */
+static double norm_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+static double norm_pdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * ORC_PI); }
+
+/* GELU, tanh form: 0.5 x (1 + tanh(c (x + 0.044715 x^3))), c = sqrt(2/pi).
+ * As 0.5 (1 + tanh(z)) = sigmoid(2 z), this is x * sigmoid(w(x)) with
+ * w(x) = 2 c (x + 0.044715 x^3), a form without cancellation at negative x. */
+static double gelu_tanh_w(double x) { return 2.0 * sqrt(2.0 / ORC_PI) * (x + 0.044715 * x * x * x); }
+static double gelu_tanh_dw(double x) { return 2.0 * sqrt(2.0 / ORC_PI) * (1.0 + 3.0 * 0.044715 * x * x); }
+
+/* act(x).  ReLU maps x <= 0 to +0 and keeps NaN. */
+double orc_act(int act, double x)
 {
-    uint16_t s = orc_bf16_round(orc_silu(orc_bf16_decode(g)));
-    return orc_bf16_round(orc_bf16_decode(s) * orc_bf16_decode(u));
+    switch (act) {
+    case ORC_ACT_SILU: return x * orc_sigmoid(x);
+    case ORC_ACT_GELU_TANH: return x * orc_sigmoid(gelu_tanh_w(x));
+    case ORC_ACT_GELU: return x * norm_cdf(x);
+    case ORC_ACT_RELU: return (x <= 0.0) ? 0.0 : x;
+    }
+    return NAN;
 }
 
-/* Backward values of one element (eager autograd of silu(g) * u). */
-static void bwd_value(uint16_t dh, uint16_t g, uint16_t u, uint16_t *dg, uint16_t *du)
+/* act'(x), the textbook derivative of each.  ReLU's is 0 for x <= 0 and 1
+ * otherwise (a NaN gate passes the gradient through, as the eager ReLU
+ * backward does: it zeroes only where its output is <= 0). */
+double orc_act_grad(int act, double x)
+{
+    switch (act) {
+    case ORC_ACT_SILU: {
+        double sig = orc_sigmoid(x);
+        return sig * (1.0 + x * (1.0 - sig));
+    }
+    case ORC_ACT_GELU_TANH: {
+        double sw = orc_sigmoid(gelu_tanh_w(x));
+        return sw + x * sw * (1.0 - sw) * gelu_tanh_dw(x);
+    }
+    case ORC_ACT_GELU: return norm_cdf(x) + x * norm_pdf(x);
+    case ORC_ACT_RELU: return (x <= 0.0) ? 0.0 : 1.0;
+    }
+    return NAN;
+}
+
+/* Forward value of one element as eager bf16 computes it: two roundings. */
+static uint16_t fwd_value(int act, uint16_t g, uint16_t u)
+{
+    uint16_t a = orc_bf16_round(orc_act(act, orc_bf16_decode(g)));
+    return orc_bf16_round(orc_bf16_decode(a) * orc_bf16_decode(u));
+}
+
+/* Backward values of one element (eager autograd of act(g) * u). */
+static void bwd_value(int act, uint16_t dh, uint16_t g, uint16_t u, uint16_t *dg, uint16_t *du)
 {
     double gv = orc_bf16_decode(g), uv = orc_bf16_decode(u), dhv = orc_bf16_decode(dh);
-    double sig = orc_sigmoid(gv);
-    uint16_t s = orc_bf16_round(gv * sig);
-    *du = orc_bf16_round(dhv * orc_bf16_decode(s));
-    uint16_t ds = orc_bf16_round(dhv * uv);
-    *dg = orc_bf16_round(orc_bf16_decode(ds) * sig * (1.0 + gv * (1.0 - sig)));
+    uint16_t a = orc_bf16_round(orc_act(act, gv));
+    *du = orc_bf16_round(dhv * orc_bf16_decode(a));
+    uint16_t da = orc_bf16_round(dhv * uv);
+    *dg = orc_bf16_round(orc_bf16_decode(da) * orc_act_grad(act, gv));
+}
+
+static int act_ok(int act) { return act >= ORC_ACT_SILU && act <= ORC_ACT_RELU; }
+
+int orc_gated_fwd_values(int act, const uint16_t *g, const uint16_t *u, int64_t n, uint16_t *h)
+{
+    if (!act_ok(act))
+        return -1;
+    for (int64_t i = 0; i < n; i++)
+        h[i] = fwd_value(act, g[i], u[i]);
+    return 0;
+}
+
+int orc_gated_bwd_values(int act, const uint16_t *dh, const uint16_t *g, const uint16_t *u,
+                         int64_t n, uint16_t *dg, uint16_t *du)
+{
+    if (!act_ok(act))
+        return -1;
+    for (int64_t i = 0; i < n; i++)
+        bwd_value(act, dh[i], g[i], u[i], &dg[i], &du[i]);
+    return 0;
 }
 
 void orc_swiglu_fwd_values(const uint16_t *g, const uint16_t *u, int64_t n, uint16_t *h)
 {
-    for (int64_t i = 0; i < n; i++)
-        h[i] = fwd_value(g[i], u[i]);
+    orc_gated_fwd_values(ORC_ACT_SILU, g, u, n, h);
 }
 
 void orc_swiglu_bwd_values(const uint16_t *dh, const uint16_t *g, const uint16_t *u,
                            int64_t n, uint16_t *dg, uint16_t *du)
 {
-    for (int64_t i = 0; i < n; i++)
-        bwd_value(dh[i], g[i], u[i], &dg[i], &du[i]);
+    orc_gated_bwd_values(ORC_ACT_SILU, dh, g, u, n, dg, du);
 }
 
 /* ------------------------------------------------------------ matrix level */
@@ -273,11 +344,11 @@ static void quant_slab(const double *y, int64_t R, int64_t W, int64_t m0,
 enum { OP_QUANT = 0, OP_FWD = 1, OP_BWD = 2 };
 
 /* Shared driver: builds the [M, W] values slab by slab, then quantizes. */
-static int run(int op, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
+static int run(int op, int act, const uint16_t *a, int64_t lda, const uint16_t *b, int64_t ldb,
                const uint16_t *c, int64_t ldc, int64_t M, int64_t N, int layout,
                const orc_out *o)
 {
-    if (M < 0 || N < 0 || layout < 1 || layout > 3)
+    if (M < 0 || N < 0 || layout < 1 || layout > 3 || !act_ok(act))
         return -1;
     if ((layout & ORC_COLWISE) && M % 32 != 0)
         return -1;
@@ -298,10 +369,10 @@ static int run(int op, const uint16_t *a, int64_t lda, const uint16_t *b, int64_
                 if (op == OP_QUANT) {
                     yr[j] = orc_bf16_decode(a[m * lda + j]);
                 } else if (op == OP_FWD) {
-                    yr[j] = orc_bf16_decode(fwd_value(a[m * lda + j], b[m * ldb + j]));
+                    yr[j] = orc_bf16_decode(fwd_value(act, a[m * lda + j], b[m * ldb + j]));
                 } else {
                     uint16_t dg, du;
-                    bwd_value(a[m * lda + j], b[m * ldb + j], c[m * ldc + j], &dg, &du);
+                    bwd_value(act, a[m * lda + j], b[m * ldb + j], c[m * ldc + j], &dg, &du);
                     yr[j] = orc_bf16_decode(dg);
                     yr[N + j] = orc_bf16_decode(du);
                 }
@@ -318,7 +389,25 @@ int orc_quant_2d(const uint16_t *x, int64_t ld_x, int64_t M, int64_t K, int layo
                  uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
 {
     orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
-    return run(OP_QUANT, x, ld_x, NULL, 0, NULL, 0, M, K, layout, &o);
+    return run(OP_QUANT, ORC_ACT_SILU, x, ld_x, NULL, 0, NULL, 0, M, K, layout, &o);
+}
+
+int orc_gated_fwd(int act, const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
+                  int64_t M, int64_t N, int layout,
+                  uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
+                  uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
+{
+    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
+    return run(OP_FWD, act, gate, ld_gate, up, ld_up, NULL, 0, M, N, layout, &o);
+}
+
+int orc_gated_bwd(int act, const uint16_t *dh, int64_t ld_dh, const uint16_t *gate, int64_t ld_gate,
+                  const uint16_t *up, int64_t ld_up, int64_t M, int64_t N, int layout,
+                  uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
+                  uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
+{
+    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
+    return run(OP_BWD, act, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout, &o);
 }
 
 int orc_swiglu_fwd(const uint16_t *gate, int64_t ld_gate, const uint16_t *up, int64_t ld_up,
@@ -326,8 +415,8 @@ int orc_swiglu_fwd(const uint16_t *gate, int64_t ld_gate, const uint16_t *up, in
                    uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
                    uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
 {
-    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
-    return run(OP_FWD, gate, ld_gate, up, ld_up, NULL, 0, M, N, layout, &o);
+    return orc_gated_fwd(ORC_ACT_SILU, gate, ld_gate, up, ld_up, M, N, layout,
+                         q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
 }
 
 int orc_swiglu_bwd(const uint16_t *dh, int64_t ld_dh, const uint16_t *gate, int64_t ld_gate,
@@ -335,8 +424,8 @@ int orc_swiglu_bwd(const uint16_t *dh, int64_t ld_dh, const uint16_t *gate, int6
                    uint8_t *q_row, int64_t ld_q_row, uint8_t *s_row, int64_t ld_s_row,
                    uint8_t *q_col, int64_t ld_q_col, uint8_t *s_col, int64_t ld_s_col)
 {
-    orc_out o = {q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col};
-    return run(OP_BWD, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout, &o);
+    return orc_gated_bwd(ORC_ACT_SILU, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout,
+                         q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
 }
 
 /* 3D per-expert colwise quant [P3, Summary]: expert e is the [N, K] matrix
