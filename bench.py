@@ -37,7 +37,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--cpu-rows", type=int, default=1024, help="rows of the workload the CPU oracle processes")
+    p.add_argument("--cpu-rows", type=int, default=2560, help="rows of the workload the CPU oracle processes")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-detail", action="store_true", help="skip the per-op breakdown")
     p.add_argument("--validate", action="store_true", help="check sampled outputs against the oracle before timing")
@@ -305,6 +305,18 @@ def run_detail(inp, fwd_out, bwd_out, stream):
             res[f"{op}_{name}"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nbytes, avg), 1),
                                    "frac": round(metrics.gbps(nbytes, avg) / metrics.HBM_PEAK_GBPS, 4)}
     print("bench: per-layout timing done", file=sys.stderr, flush=True)
+    # the other gated activations, both layouts in one pass, same inputs
+    for act in ("gelu_tanh", "gelu", "relu"):
+        f = lambda: mx.mxfp8_gated_fwd(inp.gate, inp.up, act=act, rowwise=True, colwise=True, out=fwd_out,
+                                       stream=stream)
+        b = lambda: mx.mxfp8_gated_bwd(inp.dh, inp.gate, inp.up, act=act, rowwise=True, colwise=True, out=bwd_out,
+                                       stream=stream)
+        for op, fn, nbytes in (("fwd", f, metrics.swiglu_fwd_bytes(M, N, mx.BOTH)),
+                               ("bwd", b, metrics.swiglu_bwd_bytes(M, N, mx.BOTH))):
+            avg, _ = time_launches(fn, 10, 2)
+            res[f"{act}_{op}_both"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nbytes, avg), 1),
+                                       "frac": round(metrics.gbps(nbytes, avg) / metrics.HBM_PEAK_GBPS, 4)}
+    print("bench: gated activations done", file=sys.stderr, flush=True)
     # the unfused two-kernel pipeline (bf16 activation written, then the plain
     # cast of it), both layouts: the pages' baseline structure
     h = torch.empty((M, N), dtype=torch.bfloat16, device=inp.gate.device)

@@ -57,10 +57,15 @@ typedef enum mxfp8_status {
     MXFP8_ERR_ALIGN = 4,    /* input or E4M3 output pointer not 16-byte aligned    */
     MXFP8_ERR_LAYOUT = 5,   /* layout flags not in {1, 2, 3}                       */
     MXFP8_ERR_OVERFLOW = 6, /* an extent overflows int64, or the grid is too large */
-    MXFP8_ERR_LAUNCH = 7    /* the HIP runtime refused the launch                  */
+    MXFP8_ERR_LAUNCH = 7,   /* the HIP runtime refused the launch                  */
+    MXFP8_ERR_ACT = 8       /* activation code not one of MXFP8_ACT_*              */
 } mxfp8_status;
 
 enum { MXFP8_ROWWISE = 1, MXFP8_COLWISE = 2, MXFP8_BOTH = 3 };
+
+/* Gate activations of the gated family h = act(gate) * up (see
+ * mxfp8_gated_fwd). */
+enum { MXFP8_ACT_SILU = 0, MXFP8_ACT_GELU_TANH = 1, MXFP8_ACT_GELU = 2, MXFP8_ACT_RELU = 3 };
 
 /*
  * Fused forward: h = silu(gate) * up, cast to MXFP8; h is never written.
@@ -99,6 +104,39 @@ mxfp8_status mxfp8_swiglu_bwd(const void *dh, int64_t ld_dh,
                               void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
                               void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
                               void *stream);
+
+/*
+ * The fused casts for other gated activations: h = act(gate) * up, with act
+ * chosen by `act` (MXFP8_ACT_*).  "Add swiglu + MXFP8 fused CuTe DSL
+ * kernel", API (the activation is a compile-time policy of one kernel
+ * source) and Follow-ups (more gated activations planned; none named).
+ * Taken here:
+ *   MXFP8_ACT_SILU       silu(g) = g sigmoid(g)  (same as mxfp8_swiglu_*)
+ *   MXFP8_ACT_GELU_TANH  0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
+ *   MXFP8_ACT_GELU       g Phi(g), Phi the standard normal cdf
+ *   MXFP8_ACT_RELU       max(g, 0) (+0 for g <= 0, NaN kept)
+ * Arguments, layouts, outputs and the [dGate | dUp] order are exactly those
+ * of mxfp8_swiglu_fwd / mxfp8_swiglu_bwd.  Values follow the same eager
+ * bf16 rounding sites with act in place of silu: a = bf16(act(g)),
+ * h = bf16(a * up); du = bf16(dh * a), da = bf16(dh * up),
+ * dg = bf16(da * act'(g)), act' the textbook derivative (ReLU's is 0 for
+ * g <= 0, 1 otherwise).  Computed in fp32; codes may differ from an exact
+ * evaluation by one E4M3 step.  An unknown `act` returns MXFP8_ERR_ACT
+ * before any other check.
+ */
+mxfp8_status mxfp8_gated_fwd(int act, const void *gate, int64_t ld_gate,
+                             const void *up, int64_t ld_up,
+                             int64_t M, int64_t N, int layout,
+                             void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                             void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                             void *stream);
+mxfp8_status mxfp8_gated_bwd(int act, const void *dh, int64_t ld_dh,
+                             const void *gate, int64_t ld_gate,
+                             const void *up, int64_t ld_up,
+                             int64_t M, int64_t N, int layout,
+                             void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                             void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                             void *stream);
 
 /*
  * Plain MXFP8 cast of a bf16 matrix x [M, K] (row stride ld_x): the

@@ -27,6 +27,10 @@ ROWWISE = 1
 COLWISE = 2
 BOTH = 3
 
+# gate activations of mxfp8_gated_fwd / mxfp8_gated_bwd (MXFP8_ACT_* in mxfp8.h)
+ACT_SILU, ACT_GELU_TANH, ACT_GELU, ACT_RELU = 0, 1, 2, 3
+ACTIVATIONS = {"silu": ACT_SILU, "gelu_tanh": ACT_GELU_TANH, "gelu": ACT_GELU, "relu": ACT_RELU}
+
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libmxfp8.so")
 
@@ -37,6 +41,8 @@ _int = ctypes.c_int
 _SIGNATURES = {
     "mxfp8_swiglu_fwd": [_p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
     "mxfp8_swiglu_bwd": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
+    "mxfp8_gated_fwd": [_int, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
+    "mxfp8_gated_bwd": [_int, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
     "mxfp8_quant_2d": [_p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
     "mxfp8_quant_3d_colwise": [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p],
     "mxfp8_swiglu_fwd_bf16": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
@@ -165,6 +171,50 @@ def mxfp8_swiglu_bwd(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, *, 
     return tuple(outs)
 
 
+def _act_code(act) -> int:
+    """Activation name ("silu", "gelu_tanh", "gelu", "relu") or MXFP8_ACT_* code."""
+    if isinstance(act, str):
+        if act not in ACTIVATIONS:
+            raise ValueError(f"unknown activation {act!r}; expected one of {sorted(ACTIVATIONS)}")
+        return ACTIVATIONS[act]
+    return int(act)
+
+
+def mxfp8_gated_fwd(gate: torch.Tensor, up: torch.Tensor, *, act="silu", rowwise: bool = True,
+                    colwise: bool = False, out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """MXFP8 cast of act(gate) * up; returns (q_row, q_col, s_row, s_col)."""
+    code = _act_code(act)
+    layout = _layout(rowwise, colwise)
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if gate.shape != up.shape or gate.device != up.device:
+        raise ValueError("gate and up must have the same shape and device")
+    M, N = gate.shape
+    outs = out if out is not None else alloc_outputs(M, N, layout, gate.device)
+    st = lib().mxfp8_gated_fwd(code, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+                               _stream(gate.device, stream))
+    _check("mxfp8_gated_fwd", st)
+    return tuple(outs)
+
+
+def mxfp8_gated_bwd(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, *, act="silu", rowwise: bool = True,
+                    colwise: bool = False, out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """MXFP8 cast of [dgate | dup] of act(gate) * up; returns (q_row, q_col, s_row, s_col) of width 2N."""
+    code = _act_code(act)
+    layout = _layout(rowwise, colwise)
+    pd, ldd = _bf16_matrix(dh, "dh")
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if not (dh.shape == gate.shape == up.shape) or not (dh.device == gate.device == up.device):
+        raise ValueError("dh, gate and up must have the same shape and device")
+    M, N = gate.shape
+    outs = out if out is not None else alloc_outputs(M, 2 * N, layout, gate.device)
+    st = lib().mxfp8_gated_bwd(code, pd, ldd, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+                               _stream(gate.device, stream))
+    _check("mxfp8_gated_bwd", st)
+    return tuple(outs)
+
+
 def mxfp8_quant_2d(x: torch.Tensor, *, rowwise: bool = True, colwise: bool = False,
                    out: Optional[Sequence[torch.Tensor]] = None, stream=None):
     """Plain MXFP8 cast of a bf16 [M, K] matrix; returns (q_row, q_col, s_row, s_col)."""
@@ -239,17 +289,17 @@ def mxfp8_swiglu_bwd_bf16(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor
     return y
 
 
-def gated_act_mxfp8_forward(gated_input: torch.Tensor, *, rowwise: bool = True, colwise: bool = False, out=None,
-                            stream=None):
+def gated_act_mxfp8_forward(gated_input: torch.Tensor, *, rowwise: bool = True, colwise: bool = False,
+                            activation="silu", out=None, stream=None):
     """Forward on the packed [M, 2N] = [gate | up] projection (the pages' API name)."""
     N = gated_input.shape[1] // 2
-    return mxfp8_swiglu_fwd(gated_input[:, :N], gated_input[:, N:], rowwise=rowwise, colwise=colwise, out=out,
-                            stream=stream)
+    return mxfp8_gated_fwd(gated_input[:, :N], gated_input[:, N:], act=activation, rowwise=rowwise,
+                           colwise=colwise, out=out, stream=stream)
 
 
 def gated_act_mxfp8_backward(grad_h: torch.Tensor, gated_input: torch.Tensor, *, rowwise: bool = True,
-                             colwise: bool = False, out=None, stream=None):
+                             colwise: bool = False, activation="silu", out=None, stream=None):
     """Backward on the packed [M, 2N] = [gate | up] projection; outputs [dgate | dup]."""
     N = gated_input.shape[1] // 2
-    return mxfp8_swiglu_bwd(grad_h, gated_input[:, :N], gated_input[:, N:], rowwise=rowwise, colwise=colwise,
-                            out=out, stream=stream)
+    return mxfp8_gated_bwd(grad_h, gated_input[:, :N], gated_input[:, N:], act=activation, rowwise=rowwise,
+                           colwise=colwise, out=out, stream=stream)

@@ -1,16 +1,20 @@
-// mx_ops.hpp -- per-chunk value producers of the three casts.
+// mx_ops.hpp -- per-chunk value producers of the casts.
 //
 // A chunk is eight consecutive columns of one row (one 16-byte load per
 // input).  Each op turns its input chunks into the bf16 values that get
 // quantized, packed two per word, entirely in registers:
-//   OpQuant: x itself (the plain cast).
-//   OpFwd:   h = bf16(bf16(silu(g)) * u)        -- two roundings, as eager bf16.
-//   OpBwd:   dg, du of h = silu(g) * u for upstream gradient dh
-//            (eager bf16 autograd): s = bf16(silu(g)), du = bf16(dh * s),
-//            ds = bf16(dh * u), dg = bf16(ds * sig * (1 + g * (1 - sig))).
+//   OpQuant:        x itself (the plain cast).
+//   GatedFwd<Act>:  h = bf16(bf16(act(g)) * u)      -- two roundings, as eager bf16.
+//   GatedBwd<Act>:  dg, du of h = act(g) * u for upstream gradient dh
+//                   (eager bf16 autograd): a = bf16(act(g)), du = bf16(dh * a),
+//                   da = bf16(dh * u), dg = bf16(da * act'(g)).
+//   OpFwd / OpBwd:  the SwiGLU pair, act = silu.
 // Source: "Add swiglu + MXFP8 fused CuTe DSL kernel", Summary (activation
-// never materialized), API ([gate | up] in, [dGate | dUp] out), Numerics
-// and tests (equal to the eager activation followed by the quantizer).
+// never materialized), API ([gate | up] in, [dGate | dUp] out; the activation
+// is a compile-time policy of one kernel source), Numerics and tests (equal
+// to the eager activation followed by the quantizer), Follow-ups (more gated
+// activations).  The page names no activation besides SiLU; GELU (exact and
+// tanh forms) and ReLU are taken here as the common gated-unit gates.
 #pragma once
 #include "mx_device.hpp"
 
@@ -21,32 +25,153 @@ struct OpQuant {
   __device__ __forceinline__ static void apply(const V4 *in, V4 *out) { out[0] = in[0]; }
 };
 
-// A gate below -80 needs the scaled sigmoid (see mx_device.hpp).  In bf16,
-// g < -80 exactly when the 16-bit pattern, read unsigned, exceeds 0xC2A0
-// (sign set, magnitude above 80); negative NaNs also land here, which is
-// harmless because the careful path propagates NaN too.
+// True when some gate of the chunk, as a 16-bit pattern read unsigned,
+// exceeds `far`: a negative gate beyond the activation's far threshold
+// (negative NaNs land here too, harmlessly: the careful forms propagate NaN).
+template <u32 far>
 __device__ __forceinline__ bool any_far(const u32 *g) {
-  u32 m = pk_max(pk_max(g[0], g[1]), pk_max(g[2], g[3]));
-  return max(m & 0xffffu, m >> 16) > 0xC2A0u;
+  if constexpr (far >= 0xFFFFu) {
+    return false;
+  } else {
+    u32 m = pk_max(pk_max(g[0], g[1]), pk_max(g[2], g[3]));
+    return max(m & 0xffffu, m >> 16) > far;
+  }
 }
 
-// silu(g) in fp32.  `careful` handles gates below -80 through e^g * 2^64.
-template <bool careful>
-__device__ __forceinline__ float silu_f(float g) {
-  float s = g * sigmoid_near(g);
-  if (careful && g < kFar) s = (g * exp_g_times_2p64(g)) * k2m64;
-  return s;
-}
+// ------------------------------------------------------------ gate policies
+// Each policy gives, in fp32 registers:
+//   act<careful>(g)        the activation (rounded to bf16 by the caller);
+//   dgate<careful>(da, g)  da * act'(g)   (rounded to bf16 by the caller);
+//   kFarBits               the bf16 pattern above which a chunk takes the
+//                          careful forms (gates so negative that the plain
+//                          fp32 forms would flush a representable result).
+// The careful forms scale the vanishing exponential by 2^64 and apply 2^-64
+// last, so the only subnormal rounding is the final one.
 
-struct OpFwd {
+// silu(g) = g * sigmoid(g); silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
+struct ActSilu {
+  static constexpr u32 kFarBits = 0xC2A0u;  // g < -80
+
+  template <bool careful>
+  __device__ __forceinline__ static float act(float g) {
+    float s = g * sigmoid_near(g);
+    if (careful && g < kFar) s = (g * exp_g_times_2p64(g)) * k2m64;
+    return s;
+  }
+
+  template <bool careful>
+  __device__ __forceinline__ static float dgate(float da, float g) {
+    const float sig = sigmoid_near(g);
+    float r = (da * sig) * (1.0f + g * (1.0f - sig));
+    // far-negative gate: sig == e^g, so dg = da * e^g * (1 + g)
+    if (careful && g < kFar) r = ((da * (1.0f + g)) * exp_g_times_2p64(g)) * k2m64;
+    return r;
+  }
+};
+
+// GELU, tanh form: 0.5 g (1 + tanh(c (g + 0.044715 g^3))), c = sqrt(2/pi),
+// written as g * sigmoid(w) with w = 2c (g + 0.044715 g^3) (the same value:
+// 0.5 (1 + tanh z) = sigmoid(2z)), which has no cancellation for g < 0.
+// Derivative: sigmoid(w) + g sigmoid(w) (1 - sigmoid(w)) w'(g).
+struct ActGeluTanh {
+  static constexpr float kC1 = 1.5957691216057308f;   // 2 sqrt(2/pi)
+  static constexpr float kC3 = 0.07135481627260025f;  // 2 sqrt(2/pi) * 0.044715
+  static constexpr u32 kFarBits = 0xC118u;            // g < -9.5 (w < -80 needs g < -9.68)
+
+  __device__ __forceinline__ static float w(float g) { return g * (kC1 + kC3 * (g * g)); }
+  __device__ __forceinline__ static float dw(float g) { return kC1 + 3.0f * kC3 * (g * g); }
+
+  template <bool careful>
+  __device__ __forceinline__ static float act(float g) {
+    const float wv = w(g);
+    float a = g * sigmoid_near(wv);
+    if (careful && wv < kFar) a = (g * exp_g_times_2p64(wv)) * k2m64;
+    return a;
+  }
+
+  template <bool careful>
+  __device__ __forceinline__ static float dgate(float da, float g) {
+    const float wv = w(g), sig = sigmoid_near(wv), d = dw(g);
+    const float t = sig * (1.0f - sig);
+    // where t is 0 the second term is 0 for finite g (g * t * d could read
+    // 0 * inf once g^2 overflows) and NaN for infinite g
+    const float term = (t == 0.0f) ? g * 0.0f : (g * t) * d;
+    float r = da * (sig + term);
+    if (careful && wv < kFar) {
+      // sigmoid(w) == e^w and 1 - sigmoid(w) == 1: dg = da e^w (1 + g w')
+      const float e = exp_g_times_2p64(wv);
+      r = (e == 0.0f) ? da * (g * 0.0f) : ((da * (1.0f + g * d)) * e) * k2m64;
+    }
+    return r;
+  }
+};
+
+// GELU, exact form: g Phi(g), Phi(g) = erfc(-g / sqrt 2) / 2 (the normal
+// cdf); derivative Phi(g) + g phi(g), phi(g) = e^(-g^2/2) / sqrt(2 pi).
+// For g < -8, Phi(g) = erfcx(-g / sqrt 2) e^(-g^2/2) / 2 with the scaled
+// complementary error function erfcx(t) = e^(t^2) erfc(t), so the vanishing
+// factor is the plain exponential, formed times 2^64.
+struct ActGelu {
+  static constexpr float kRsqrt2 = 0.7071067811865476f;
+  static constexpr float kRsqrt2Pi = 0.3989422804014327f;  // 1 / sqrt(2 pi)
+  static constexpr float kFarG = -8.0f;
+  static constexpr u32 kFarBits = 0xC100u;  // g < -8
+
+  // e^(-g^2/2) (g^2 is exact for a bf16 g)
+  __device__ __forceinline__ static float gauss(float g) {
+    return __builtin_amdgcn_exp2f((-0.5f * (g * g)) * kLog2e);
+  }
+  __device__ __forceinline__ static float gauss_times_2p64(float g) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(-0.5f * (g * g), kLog2e, 64.0f));
+  }
+
+  template <bool careful>
+  __device__ __forceinline__ static float act(float g) {
+    float a = g * (0.5f * erfcf(-g * kRsqrt2));
+    if (careful && g < kFarG) a = ((g * (0.5f * erfcxf(-g * kRsqrt2))) * gauss_times_2p64(g)) * k2m64;
+    return a;
+  }
+
+  template <bool careful>
+  __device__ __forceinline__ static float dgate(float da, float g) {
+    float r = da * (0.5f * erfcf(-g * kRsqrt2) + g * (kRsqrt2Pi * gauss(g)));
+    if (careful && g < kFarG) {
+      const float e = gauss_times_2p64(g);
+      r = (e == 0.0f) ? da * (g * 0.0f)
+                      : ((da * (0.5f * erfcxf(-g * kRsqrt2) + g * kRsqrt2Pi)) * e) * k2m64;
+    }
+    return r;
+  }
+};
+
+// ReLU: g for g > 0, +0 otherwise (NaN stays NaN); derivative 0 for g <= 0
+// and 1 otherwise, so a NaN gate passes the gradient through as eager's
+// threshold backward does.
+struct ActRelu {
+  static constexpr u32 kFarBits = 0xFFFFu;  // no careful form needed
+
+  template <bool careful>
+  __device__ __forceinline__ static float act(float g) {
+    return g <= 0.0f ? 0.0f : g;
+  }
+
+  template <bool careful>
+  __device__ __forceinline__ static float dgate(float da, float g) {
+    return g <= 0.0f ? da * 0.0f : da;
+  }
+};
+
+// ------------------------------------------------------------------ gated ops
+template <class Act>
+struct GatedFwd {
   static constexpr int IN = 2, OUT = 1;  // in: gate, up
 
   template <bool careful>
   __device__ __forceinline__ static void eval(const u32 *g, const u32 *u, u32 *h) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      u32 sp = pack_bf16(silu_f<careful>(lo_f(g[k])), silu_f<careful>(hi_f(g[k])));
-      h[k] = pack_bf16(lo_f(sp) * lo_f(u[k]), hi_f(sp) * hi_f(u[k]));
+      u32 ap = pack_bf16(Act::template act<careful>(lo_f(g[k])), Act::template act<careful>(hi_f(g[k])));
+      h[k] = pack_bf16(lo_f(ap) * lo_f(u[k]), hi_f(ap) * hi_f(u[k]));
     }
   }
 
@@ -56,23 +181,20 @@ struct OpFwd {
     eval<false>(g, u, h);
     // rare: redo the whole chunk from the packed inputs, so only packed
     // words are live across the branch
-    if (__builtin_expect(any_far(g), 0)) eval<true>(g, u, h);
+    if (__builtin_expect(any_far<Act::kFarBits>(g), 0)) eval<true>(g, u, h);
   }
 };
 
-struct OpBwd {
+template <class Act>
+struct GatedBwd {
   static constexpr int IN = 3, OUT = 2;  // in: dh, gate, up; out: dgate, dup
 
   template <bool careful>
   __device__ __forceinline__ static void elem(float dhv, float gv, float uv, float &dg, float &du) {
-    const float sig = sigmoid_near(gv);
-    const float s = round_bf16(silu_f<careful>(gv));
-    du = dhv * s;
-    const float ds = round_bf16(dhv * uv);
-    float r = (ds * sig) * (1.0f + gv * (1.0f - sig));
-    // far-negative gate: sig == e^g, so dg = ds * e^g * (1 + g); 2^-64 last
-    if (careful && gv < kFar) r = ((ds * (1.0f + gv)) * exp_g_times_2p64(gv)) * k2m64;
-    dg = r;
+    const float a = round_bf16(Act::template act<careful>(gv));
+    du = dhv * a;
+    const float da = round_bf16(dhv * uv);
+    dg = Act::template dgate<careful>(da, gv);
   }
 
   template <bool careful>
@@ -91,8 +213,12 @@ struct OpBwd {
     const u32 *dh = &in[0].x, *g = &in[1].x, *u = &in[2].x;
     u32 *dg = &out[0].x, *du = &out[1].x;
     eval<false>(dh, g, u, dg, du);
-    if (__builtin_expect(any_far(g), 0)) eval<true>(dh, g, u, dg, du);
+    if (__builtin_expect(any_far<Act::kFarBits>(g), 0)) eval<true>(dh, g, u, dg, du);
   }
 };
+
+// The SwiGLU pair under names of their own (kernel symbols stay short).
+struct OpFwd : GatedFwd<ActSilu> {};
+struct OpBwd : GatedBwd<ActSilu> {};
 
 }  // namespace mx

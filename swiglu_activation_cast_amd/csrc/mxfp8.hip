@@ -5,8 +5,9 @@
 // enqueues it on the caller's stream.  Nothing is allocated, synchronized
 // or read back.  API shape: "Add swiglu + MXFP8 fused CuTe DSL kernel",
 // API (forward/backward with rowwise/colwise switches, fixed-arity
-// outputs) and Numerics and tests (launcher guards on sizes and pointer
-// alignment, each error path reachable without a device).
+// outputs; one kernel source per activation) and Numerics and tests
+// (launcher guards on sizes and pointer alignment, each error path reachable
+// without a device).
 #include <hip/hip_runtime.h>
 #include <algorithm>
 #include <limits.h>
@@ -35,6 +36,8 @@ bool extent_ok(int64_t rows, int64_t cols, int64_t ld) {
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool act_ok(int act) { return act >= MXFP8_ACT_SILU && act <= MXFP8_ACT_RELU; }
 
 // The colwise kernel addresses each tile from a wave-uniform base with
 // 32-bit per-lane offsets that reach (tile rows - 1) input / q_row / s_row
@@ -192,30 +195,58 @@ Args make_args(const void *const *in, const int64_t *ld_in, int n_in, int64_t M,
 
 extern "C" {
 
-mxfp8_status mxfp8_swiglu_fwd(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
-                              int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
-                              int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
-                              void *stream) {
+mxfp8_status mxfp8_gated_fwd(int act, const void *gate, int64_t ld_gate, const void *up, int64_t ld_up,
+                             int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
+                             int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                             void *stream) {
+  if (!act_ok(act)) return MXFP8_ERR_ACT;
   const void *in[2] = {gate, up};
   const int64_t ld[2] = {ld_gate, ld_up};
   mxfp8_status st = check_2d(Kind::Fwd, in, ld, 2, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
                              ld_q_col, s_col, ld_s_col);
   if (st != MXFP8_OK || M == 0 || N == 0) return st;
   Args a = make_args(in, ld, 2, M, N, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
-  return dispatch_2d<mx::OpFwd>(a, layout, stream);
+  switch (act) {
+    case MXFP8_ACT_SILU: return dispatch_2d<mx::OpFwd>(a, layout, stream);
+    case MXFP8_ACT_GELU_TANH: return dispatch_2d<mx::GatedFwd<mx::ActGeluTanh>>(a, layout, stream);
+    case MXFP8_ACT_GELU: return dispatch_2d<mx::GatedFwd<mx::ActGelu>>(a, layout, stream);
+    default: return dispatch_2d<mx::GatedFwd<mx::ActRelu>>(a, layout, stream);
+  }
 }
 
-mxfp8_status mxfp8_swiglu_bwd(const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate, const void *up,
-                              int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row,
-                              void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col,
-                              int64_t ld_s_col, void *stream) {
+mxfp8_status mxfp8_gated_bwd(int act, const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate,
+                             const void *up, int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row,
+                             int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                             void *s_col, int64_t ld_s_col, void *stream) {
+  if (!act_ok(act)) return MXFP8_ERR_ACT;
   const void *in[3] = {dh, gate, up};
   const int64_t ld[3] = {ld_dh, ld_gate, ld_up};
   mxfp8_status st = check_2d(Kind::Bwd, in, ld, 3, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
                              ld_q_col, s_col, ld_s_col);
   if (st != MXFP8_OK || M == 0 || N == 0) return st;
   Args a = make_args(in, ld, 3, M, N, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
-  return dispatch_2d<mx::OpBwd>(a, layout, stream);
+  switch (act) {
+    case MXFP8_ACT_SILU: return dispatch_2d<mx::OpBwd>(a, layout, stream);
+    case MXFP8_ACT_GELU_TANH: return dispatch_2d<mx::GatedBwd<mx::ActGeluTanh>>(a, layout, stream);
+    case MXFP8_ACT_GELU: return dispatch_2d<mx::GatedBwd<mx::ActGelu>>(a, layout, stream);
+    default: return dispatch_2d<mx::GatedBwd<mx::ActRelu>>(a, layout, stream);
+  }
+}
+
+mxfp8_status mxfp8_swiglu_fwd(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
+                              int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
+                              int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                              void *stream) {
+  return mxfp8_gated_fwd(MXFP8_ACT_SILU, gate, ld_gate, up, ld_up, M, N, layout, q_row, ld_q_row, s_row, ld_s_row,
+                         q_col, ld_q_col, s_col, ld_s_col, stream);
+}
+
+mxfp8_status mxfp8_swiglu_bwd(const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate, const void *up,
+                              int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row,
+                              void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col,
+                              int64_t ld_s_col, void *stream) {
+  return mxfp8_gated_bwd(MXFP8_ACT_SILU, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout, q_row, ld_q_row, s_row,
+                         ld_s_row, q_col, ld_q_col, s_col, ld_s_col, stream);
 }
 
 mxfp8_status mxfp8_quant_2d(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout, void *q_row,
@@ -290,6 +321,7 @@ const char *mxfp8_status_str(mxfp8_status status) {
     case MXFP8_ERR_LAYOUT: return "layout must be rowwise (1), colwise (2) or both (3)";
     case MXFP8_ERR_OVERFLOW: return "sizes overflow the addressable range or the launch grid";
     case MXFP8_ERR_LAUNCH: return "the HIP runtime refused the kernel launch";
+    case MXFP8_ERR_ACT: return "activation must be MXFP8_ACT_SILU, _GELU_TANH, _GELU or _RELU";
   }
   return "unknown status";
 }

@@ -14,7 +14,7 @@ import pytest
 import swiglu_activation_cast_amd as mx
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, STRIDE, ALIGN, LAYOUT, OVERFLOW, LAUNCH = range(8)
+OK, NULL, SHAPE, STRIDE, ALIGN, LAYOUT, OVERFLOW, LAUNCH, ACT = range(9)
 
 A = 1 << 20  # a fake, 16-byte aligned "device address" (never dereferenced)
 
@@ -28,14 +28,15 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mx.lib()
     names = declared_functions()
-    assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_quant_2d", "mxfp8_quant_3d_colwise",
-                     "mxfp8_swiglu_fwd_bf16", "mxfp8_swiglu_bwd_bf16", "mxfp8_status_str"}
+    assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_gated_fwd", "mxfp8_gated_bwd",
+                     "mxfp8_quant_2d", "mxfp8_quant_3d_colwise", "mxfp8_swiglu_fwd_bf16", "mxfp8_swiglu_bwd_bf16",
+                     "mxfp8_status_str"}
     for n in names:
         assert getattr(lib, n) is not None
 
 
 def test_status_strings():
-    for st in range(8):
+    for st in range(9):
         assert len(mx.status_str(st)) >= 2
     assert mx.status_str(99) == "unknown status"
 
@@ -56,6 +57,24 @@ def bwd(**kw):
     return mx.lib().mxfp8_swiglu_bwd(a["dh"], a["ld_dh"], a["gate"], a["ld_gate"], a["up"], a["ld_up"], a["M"],
                                      a["N"], a["layout"], a["q_row"], a["ld_q_row"], a["s_row"], a["ld_s_row"],
                                      a["q_col"], a["ld_q_col"], a["s_col"], a["ld_s_col"], None)
+
+
+def gfwd(act=0, **kw):
+    a = dict(gate=A, ld_gate=256, up=A + 256, ld_up=256, M=64, N=128, layout=3,
+             q_row=A, ld_q_row=128, s_row=A, ld_s_row=4, q_col=A, ld_q_col=64, s_col=A, ld_s_col=2)
+    a.update(kw)
+    return mx.lib().mxfp8_gated_fwd(act, a["gate"], a["ld_gate"], a["up"], a["ld_up"], a["M"], a["N"], a["layout"],
+                                    a["q_row"], a["ld_q_row"], a["s_row"], a["ld_s_row"], a["q_col"],
+                                    a["ld_q_col"], a["s_col"], a["ld_s_col"], None)
+
+
+def gbwd(act=0, **kw):
+    a = dict(dh=A, ld_dh=128, gate=A, ld_gate=256, up=A + 256, ld_up=256, M=64, N=128, layout=3,
+             q_row=A, ld_q_row=256, s_row=A, ld_s_row=8, q_col=A, ld_q_col=64, s_col=A, ld_s_col=2)
+    a.update(kw)
+    return mx.lib().mxfp8_gated_bwd(act, a["dh"], a["ld_dh"], a["gate"], a["ld_gate"], a["up"], a["ld_up"], a["M"],
+                                    a["N"], a["layout"], a["q_row"], a["ld_q_row"], a["s_row"], a["ld_s_row"],
+                                    a["q_col"], a["ld_q_col"], a["s_col"], a["ld_s_col"], None)
 
 
 def q2d(**kw):
@@ -194,3 +213,35 @@ def test_bf16_value_entry_points_errors():
     assert b(A, 128, A, 128, None, 128, 64, 128, A, 256, None) == NULL
     assert b(A, 128, A, 128, A, 128, 64, 128, A + 4, 256, None) == ALIGN
 
+
+
+@pytest.mark.parametrize("call", [gfwd, gbwd])
+def test_gated_activation_errors(call):
+    # an unknown activation is refused before any other check, even on an
+    # empty or otherwise invalid call
+    for act in (-1, 4, 99):
+        assert call(act=act) == ACT
+        assert call(act=act, M=0) == ACT
+        assert call(act=act, layout=0) == ACT
+
+
+@pytest.mark.parametrize("call", [gfwd, gbwd])
+@pytest.mark.parametrize("act", [0, 1, 2, 3])
+def test_gated_checks_match_swiglu(call, act):
+    """Every activation runs the same argument checks as the SwiGLU calls."""
+    plain = fwd if call is gfwd else bwd
+    cases = [dict(layout=0), dict(M=-1), dict(N=48), dict(M=40, layout=2), dict(gate=None), dict(ld_gate=64),
+             dict(ld_q_row=136), dict(gate=A + 2), dict(q_col=A + 1), dict(layout=3, ld_q_row=1 << 25)]
+    for kw in cases:
+        assert call(act=act, **kw) == plain(**kw), kw
+    nul = dict(q_row=None, s_row=None, q_col=None, s_col=None)
+    assert call(act=act, M=0, gate=None, up=None, **nul) == OK
+
+
+def test_binding_activation_names():
+    assert mx.ACTIVATIONS == {"silu": 0, "gelu_tanh": 1, "gelu": 2, "relu": 3}
+    from swiglu_activation_cast_amd._binding import _act_code
+
+    with pytest.raises(ValueError):
+        _act_code("swish")
+    assert _act_code("gelu") == 2 and _act_code(3) == 3
