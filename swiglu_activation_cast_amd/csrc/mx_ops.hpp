@@ -108,38 +108,60 @@ struct ActGeluTanh {
 
 // GELU, exact form: g Phi(g), Phi(g) = erfc(-g / sqrt 2) / 2 (the normal
 // cdf); derivative Phi(g) + g phi(g), phi(g) = e^(-g^2/2) / sqrt(2 pi).
-// For g < -8, Phi(g) = erfcx(-g / sqrt 2) e^(-g^2/2) / 2 with the scaled
-// complementary error function erfcx(t) = e^(t^2) erfc(t), so the vanishing
-// factor is the plain exponential, formed times 2^64.
+//
+// erfc(z) for z = |g| / sqrt 2 >= 0 is t e^(-z^2 + P(x)) with t = 2 / (2 + z)
+// and x = 2t - 1: the change of variable of Schonfelder's Chebyshev
+// expansions of the error function, which maps z in [0, inf) onto x in
+// (-1, 1], where P(x) = ln(erfcx(z) (2 + z) / 2) is smooth.  P is the degree-9
+// least-squares fit printed by gen_erfc_fit.py (fit error 1.0e-7 absolute in
+// P, so relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
+// exact for a bf16 g, so e^(-z^2 + P) is a single exponential; Phi(g) is
+// erfc(z) / 2 for g < 0 and 1 - erfc(z) / 2 otherwise.  For g < -8 the
+// exponentials are formed times 2^64 (2^-64 applied last).
+constexpr float kErfcP[10] = {-0x1.57f564p-1f, 0x1.58649p-1f, 0x1.83d5bp-5f, -0x1.7fffc4p-5f, -0x1.438b2ep-7f,
+                              0x1.1d34dep-7f, 0x1.d1b74cp-10f, -0x1.0c8826p-9f, -0x1.b404a2p-13f, 0x1.5df29ep-12f};
+
 struct ActGelu {
   static constexpr float kRsqrt2 = 0.7071067811865476f;
   static constexpr float kRsqrt2Pi = 0.3989422804014327f;  // 1 / sqrt(2 pi)
   static constexpr float kFarG = -8.0f;
   static constexpr u32 kFarBits = 0xC100u;  // g < -8
 
-  // e^(-g^2/2) (g^2 is exact for a bf16 g)
-  __device__ __forceinline__ static float gauss(float g) {
-    return __builtin_amdgcn_exp2f((-0.5f * (g * g)) * kLog2e);
+  // erfc(|g| / sqrt 2) / 2, times 2^64 when `scaled`
+  template <bool scaled>
+  __device__ __forceinline__ static float half_erfc(float g) {
+    const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
+    const float x = __builtin_fmaf(th, 4.0f, -1.0f);
+    float p = kErfcP[9];
+#pragma unroll
+    for (int i = 8; i >= 0; i--) p = __builtin_fmaf(p, x, kErfcP[i]);
+    const float e = __builtin_fmaf(-0.5f * g, g, p);  // -z^2 + P(x)
+    return th * __builtin_amdgcn_exp2f(scaled ? __builtin_fmaf(e, kLog2e, 64.0f) : e * kLog2e);
   }
-  __device__ __forceinline__ static float gauss_times_2p64(float g) {
-    return __builtin_amdgcn_exp2f(__builtin_fmaf(-0.5f * (g * g), kLog2e, 64.0f));
+
+  __device__ __forceinline__ static float cdf(float g) {
+    const float q = half_erfc<false>(g);
+    return g < 0.0f ? q : 1.0f - q;
+  }
+
+  // e^(-g^2/2) (g^2 is exact for a bf16 g), times 2^64 when `scaled`
+  template <bool scaled>
+  __device__ __forceinline__ static float gauss(float g) {
+    const float h = -0.5f * (g * g);
+    return __builtin_amdgcn_exp2f(scaled ? __builtin_fmaf(h, kLog2e, 64.0f) : h * kLog2e);
   }
 
   template <bool careful>
   __device__ __forceinline__ static float act(float g) {
-    float a = g * (0.5f * erfcf(-g * kRsqrt2));
-    if (careful && g < kFarG) a = ((g * (0.5f * erfcxf(-g * kRsqrt2))) * gauss_times_2p64(g)) * k2m64;
+    float a = g * cdf(g);
+    if (careful && g < kFarG) a = (g * half_erfc<true>(g)) * k2m64;
     return a;
   }
 
   template <bool careful>
   __device__ __forceinline__ static float dgate(float da, float g) {
-    float r = da * (0.5f * erfcf(-g * kRsqrt2) + g * (kRsqrt2Pi * gauss(g)));
-    if (careful && g < kFarG) {
-      const float e = gauss_times_2p64(g);
-      r = (e == 0.0f) ? da * (g * 0.0f)
-                      : ((da * (0.5f * erfcxf(-g * kRsqrt2) + g * kRsqrt2Pi)) * e) * k2m64;
-    }
+    float r = da * (cdf(g) + g * (kRsqrt2Pi * gauss<false>(g)));
+    if (careful && g < kFarG) r = (da * (half_erfc<true>(g) + g * (kRsqrt2Pi * gauss<true>(g)))) * k2m64;
     return r;
   }
 };

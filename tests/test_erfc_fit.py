@@ -1,0 +1,88 @@
+"""The exact-GELU gate's erfc polynomial (host-side checks, no GPU).
+
+- The constants in csrc/mx_ops.hpp are exactly what gen_erfc_fit.py prints.
+- The kernel's float32 evaluation, emulated step by step in numpy float32,
+  stays within 1e-5 relative of the normal cdf (scipy) for GELU's value
+  over every finite bf16 gate whose result is a normal float, and within a
+  small absolute error for the derivative.  (The hardware exp2 and
+  reciprocal carry about one ulp more than numpy's correctly rounded ones;
+  the bounds leave room for that.)
+"""
+import importlib.util
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "swiglu_activation_cast_amd", "csrc")
+
+scipy_special = pytest.importorskip("scipy.special")
+
+
+def _gen():
+    spec = importlib.util.spec_from_file_location("gen_erfc_fit", os.path.join(CSRC, "gen_erfc_fit.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def header_coefficients():
+    text = open(os.path.join(CSRC, "mx_ops.hpp")).read()
+    m = re.search(r"kErfcP\[(\d+)\]\s*=\s*\{([^}]*)\}", text)
+    assert m, "kErfcP not found in mx_ops.hpp"
+    lits = [s.strip() for s in m.group(2).split(",")]
+    assert len(lits) == int(m.group(1))
+    return lits
+
+
+def test_header_constants_are_the_generated_fit():
+    gen = _gen()
+    assert header_coefficients() == gen.c_literals()
+    _, err = gen.fit()
+    assert err < 2e-7
+
+
+def _emulate(coeffs, g):
+    """float32 steps of ActGelu: (act, derivative), each already rescaled."""
+    f32 = np.float32
+    c = [f32(float.fromhex(s.rstrip("f"))) for s in coeffs]
+    l2e = f32(1.4426950408889634)
+    with np.errstate(all="ignore"):
+        far = g < f32(-8.0)
+        sc = np.where(far, f32(64.0), f32(0.0)).astype(f32)
+        th = (f32(1.0) / (f32(2.0) + np.abs(g) * f32(0.7071067811865476))).astype(f32)
+        x = (th * f32(4.0) - f32(1.0)).astype(f32)
+        p = np.full_like(x, c[-1])
+        for ci in c[-2::-1]:
+            p = (p * x + ci).astype(f32)
+        e = ((f32(-0.5) * g) * g + p).astype(f32)
+        q = (th * np.exp2((e * l2e + sc).astype(f32))).astype(f32)
+        cdf = np.where(g < 0, q, f32(1.0) - q).astype(f32)
+        gauss = np.exp2((((f32(-0.5) * (g * g)) * l2e) + sc).astype(f32)).astype(f32)
+        act = (g * cdf).astype(np.float64)
+        grad = (cdf + g * (f32(0.3989422804014327) * gauss)).astype(np.float64)
+    scale = np.where(far, 2.0 ** -64, 1.0)
+    return act * scale, grad * scale
+
+
+def test_float32_evaluation_error_over_every_bf16_gate():
+    bits = np.arange(65536, dtype=np.uint32)
+    g = (bits << 16).view(np.float32)
+    g = g[np.isfinite(g)]
+    act, grad = _emulate(header_coefficients(), g)
+    gd = g.astype(np.float64)
+    cdf = scipy_special.ndtr(gd)
+    want_act = gd * cdf
+    want_grad = cdf + gd * np.exp(-0.5 * gd * gd) / np.sqrt(2.0 * np.pi)
+    m = np.abs(want_act) > 1e-37
+    rel = np.abs(act[m] - want_act[m]) / np.abs(want_act[m])
+    assert rel.max() < 1e-5, rel.max()
+    # below the normal range the result is a bf16 subnormal at most: absolute
+    tiny = ~m
+    assert np.abs(act[tiny] - want_act[tiny]).max() < 1e-42
+    # the derivative crosses zero near g = -0.75: absolute error there
+    err = np.abs(grad - want_grad) / np.maximum(np.abs(want_grad), 1e-3)
+    ok = np.abs(want_grad) > 1e-37
+    assert err[ok].max() < 1e-4, err[ok].max()
