@@ -16,10 +16,12 @@ ARCH = "gfx950"
 
 
 def kernel_source_hash() -> str:
-    """Short hash of the kernel sources (every file under csrc/): ties a
-    recorded profile to the code it measured."""
+    """Short hash of the kernel sources (the .hip/.hpp/.h files under
+    csrc/): ties a recorded profile to the code it measured."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
+        if not name.endswith((".hip", ".hpp", ".h")):
+            continue
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
