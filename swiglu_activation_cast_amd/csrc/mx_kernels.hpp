@@ -219,6 +219,12 @@ constexpr int kG = kTM / 16;            // 16-row groups per tile column
 static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0 && (kTC * kG) % kNT == 0, "tile shape");
 
 
+// Static LDS of k_tiled<Op, *>: one transposed bf16 tile per output half.
+template <class Op>
+constexpr size_t tiled_lds_bytes() {
+  return (size_t)Op::OUT * kTC * kRS * sizeof(uint16_t);
+}
+
 #ifndef MX_MIN_WAVES
 #define MX_MIN_WAVES 1
 #endif

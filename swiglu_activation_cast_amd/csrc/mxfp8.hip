@@ -103,19 +103,39 @@ mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, in
   return MXFP8_OK;
 }
 
-mxfp8_status launch(const void *kernel, int64_t blocks, int threads, const Args &a, void *stream) {
+mxfp8_status launch(const void *kernel, int64_t blocks, int threads, const Args &a, void *stream,
+                    unsigned dyn_lds = 0) {
   // Grid x is limited to 2^32 - 1 work-items; keep well inside it.
   if (blocks <= 0 || blocks > (int64_t)INT32_MAX / threads) return MXFP8_ERR_OVERFLOW;
   Args copy = a;
   void *kargs[] = {&copy};
-  hipError_t err = hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), kargs, 0, (hipStream_t)stream);
+  hipError_t err =
+      hipLaunchKernel(kernel, dim3((unsigned)blocks), dim3(threads), kargs, dyn_lds, (hipStream_t)stream);
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
+// Occupancy cap of a colwise-only launch.  The tiled kernel's own LDS lets
+// four workgroups share a CU (two for the backward, whose tile holds both
+// output halves).  On the largest grids fewer tiles in flight per XCD stream
+// faster (MI355X, colwise-only): the 2D casts at 131072 x 8192 run 2-3% faster
+// at two workgroups per CU, the 3D cast of 16 or 64 experts of 8192 x 5120 1%
+// faster at three; smaller grids lose from it.  The cap is applied by
+// requesting dynamic LDS that the kernel does not touch: with 160 KiB of LDS
+// per CU, more than 160 KiB / (cap + 1) per workgroup leaves room for `cap`.
+constexpr int64_t kLdsPerCu = 160 * 1024;
+constexpr int64_t kCapTiles2d = 32768, kCapTiles3d = 40960;  // grid sizes where the caps were measured to pay
+
+unsigned lds_pad_for_cap(int cap, size_t static_lds) {
+  if (cap <= 0) return 0;
+  const int64_t pad = kLdsPerCu / (cap + 1) + 1 - (int64_t)static_lds;
+  return pad <= 0 ? 0u : (unsigned)((pad + 1023) / 1024 * 1024);
+}
+
 // Launch of the colwise / both-layout kernel over `batches` stacked [M, N]
-// problems (batches > 1 only for the 3D cast).
+// problems (batches > 1 only for the 3D cast); `cap` is the workgroups per
+// CU for a colwise-only launch (0: as many as fit).
 template <class Op>
-mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream) {
+mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, int cap = 0) {
   const int64_t n_rt = (a.M + mx::kTM - 1) / mx::kTM, n_ct = (a.N + mx::kTC - 1) / mx::kTC;
   if (n_rt > INT32_MAX || n_ct > INT32_MAX) return MXFP8_ERR_OVERFLOW;
   a.n_rt = (int32_t)n_rt;
@@ -125,7 +145,8 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream) {
   const void *k = rows ? (const void *)&mx::k_tiled<Op, true> : (const void *)&mx::k_tiled<Op, false>;
   // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
   a.band = (int32_t)std::min<int64_t>(rows ? kBandBoth : kBandCol, n_rt);
-  return launch(k, blocks, mx::kNT, a, stream);
+  const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op>());
+  return launch(k, blocks, mx::kNT, a, stream, pad);
 }
 
 // Checks of the bf16 value entry points: inputs as for the fused calls,
@@ -167,7 +188,8 @@ mxfp8_status dispatch_2d(const Args &a, int layout, void *stream) {
     const int64_t blocks = (a.M + mx::kRowWaves - 1) / mx::kRowWaves;
     return launch((const void *)&mx::k_rowwise<Op, kRowUnroll>, blocks, 256, a, stream);
   }
-  return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream);
+  const int64_t tiles = ((a.M + mx::kTM - 1) / mx::kTM) * ((a.N + mx::kTC - 1) / mx::kTC);
+  return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream, tiles >= kCapTiles2d ? 2 : 0);
 }
 
 Args make_args(const void *const *in, const int64_t *ld_in, int n_in, int64_t M, int64_t N, void *q_row,
@@ -287,7 +309,8 @@ mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t
   a.bstride_in = stride_e;
   a.bstride_q = K * N;
   a.bstride_s = K * (N / 32);
-  return launch_colwise<mx::OpQuant>(a, false, E, stream);
+  const int64_t tiles = E * ((N + mx::kTM - 1) / mx::kTM) * ((K + mx::kTC - 1) / mx::kTC);
+  return launch_colwise<mx::OpQuant>(a, false, E, stream, tiles >= kCapTiles3d ? 3 : 0);
 }
 
 mxfp8_status mxfp8_swiglu_fwd_bf16(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
