@@ -150,7 +150,7 @@ def traffic(fetch_dir, write_dir, workload, experts, command, out, kernel="bwd_b
         f.write("\n".join(lines) + "\n")
 
 
-def stats(csv_path, workload, experts, command, out, top=14):
+def stats(csv_path, workload, experts, command, out, top=24):
     with open(csv_path) as f:
         rows = list(csv.DictReader(f))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
