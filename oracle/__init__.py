@@ -69,6 +69,7 @@ def _load():
         "orc_swiglu_fwd": (ctypes.c_int, [_p, _i64, _p, _i64, _i64, _i64, ctypes.c_int] + [_p, _i64] * 4),
         "orc_swiglu_bwd": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int] + [_p, _i64] * 4),
         "orc_quant_3d_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _i64, _p, _p]),
+        "orc_mx_gemm": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -283,3 +284,31 @@ def quant_3d_colwise(w):
         "quant_3d_colwise",
     )
     return q, s
+
+
+# ------------------------------------------------------------- MX GEMM
+def _u8_mat(x) -> tuple[np.ndarray, int]:
+    x = np.asarray(x)
+    if x.dtype != np.uint8 or x.ndim != 2:
+        raise TypeError("expected a 2-D uint8 array")
+    if x.strides[1] != 1 or x.strides[0] < x.shape[1]:
+        x = np.ascontiguousarray(x)
+    return x, x.strides[0]
+
+
+def mx_gemm(a, sa, b, sb):
+    """C = A B^T of MXFP8 operands stored K-contiguous: a [M, K] and b [N, K]
+    E4M3 codes with E8M0 scales sa [M, K/32], sb [N, K/32].  Returns (C,
+    sum |products|), both float64 [M, N]."""
+    a, lda = _u8_mat(a)
+    b, ldb = _u8_mat(b)
+    sa, ld_sa = _u8_mat(sa)
+    sb, ld_sb = _u8_mat(sb)
+    M, K = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == K and sa.shape == (M, K // 32) and sb.shape == (N, K // 32)
+    c = np.zeros((M, N), np.float64)
+    cabs = np.zeros((M, N), np.float64)
+    _check(_load().orc_mx_gemm(_ptr(a), lda, _ptr(sa), ld_sa, _ptr(b), ldb, _ptr(sb), ld_sb, M, N, K,
+                               _ptr(c), N, _ptr(cabs), N), "mx_gemm")
+    return c, cabs

@@ -22,7 +22,8 @@
  *       single input/output TMA descriptors", Summary: the 3D (E,N,K)
  *       colwise quant writes each expert column-major.
  *  [P4] "[mxfp8 moe training] add compile support", Perf analysis: the 2D
- *       colwise ("dim1") cast output is column-major.
+ *       colwise ("dim1") cast output is column-major; the cast outputs feed
+ *       a scaled grouped GEMM (the consumer, orc_mx_gemm below).
  *
  * Readings where the pages are silent (each one is listed in the design
  * notes of the repository):
@@ -46,6 +47,9 @@
  *    ReLU, each in place of silu with the same rounding sites:
  *    a = bf16(act(g)), h = bf16(a * u); du = bf16(dh * a),
  *    da = bf16(dh * u), dg = bf16(da * act'(g)).
+ *  - The consumer GEMM is C = A B^T with both operands K-contiguous (as the
+ *    rowwise output, or the colwise output of the transposed operand,
+ *    stores them) and each element worth decode(code) * 2^(scale - 127).
  *
  * All real arithmetic here is IEEE double: a product of two bf16 values is
  * exact in double, and silu/sigmoid carry ~1e-16 relative error before the
@@ -449,5 +453,55 @@ int orc_quant_3d_colwise(const uint16_t *w, int64_t E, int64_t N, int64_t K,
                                 s + e * K * (N / 32) + k * (N / 32) + n0 / 32);
             }
     free(blk);
+    return 0;
+}
+
+/* ------------------------------------------------------ MX GEMM (consumer) */
+
+/* The consumer of the casts: C = A B^T with both operands MXFP8 and stored
+ * with K contiguous, as the casts emit them (rowwise output of [M, K] and
+ * of [N, K], or the colwise output, whose rows run along the blocked axis).
+ * [P4, Perf analysis] feeds such operands to a scaled (grouped) GEMM;
+ * [P1, Summary] casts for exactly that consumer.
+ *   a  [M, K] E4M3 codes, row stride lda;  sa [M, K/32] E8M0, row stride ld_sa
+ *   b  [N, K] E4M3 codes, row stride ldb;  sb [N, K/32] E8M0, row stride ld_sb
+ * Every element stands for decode(code) * 2^(scale - 127) (NaN for the NaN
+ * codes or scale byte 255); C[m][n] is the plain sum over k of products of
+ * those values, in double (each product is exact), and cabs[m][n] the sum
+ * of their magnitudes (the scale of the rounding error any summation order
+ * can make).  K must be a multiple of 32. */
+static void mx_row_values(const uint8_t *q, const uint8_t *s, int64_t K, double *out)
+{
+    for (int64_t k = 0; k < K; k++)
+        out[k] = orc_e4m3_decode(q[k]) * orc_e8m0_decode(s[k / 32]);
+}
+
+int orc_mx_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa,
+                const uint8_t *b, int64_t ldb, const uint8_t *sb, int64_t ld_sb,
+                int64_t M, int64_t N, int64_t K, double *c, int64_t ldc, double *cabs, int64_t ld_cabs)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 32 != 0)
+        return -1;
+    double *bv = (double *)malloc(sizeof(double) * (size_t)(N * K + K + 1));
+    if (!bv)
+        return -2;
+    double *av = bv + N * K;
+    for (int64_t n = 0; n < N; n++)
+        mx_row_values(b + n * ldb, sb + n * ld_sb, K, bv + n * K);
+    for (int64_t m = 0; m < M; m++) {
+        mx_row_values(a + m * lda, sa + m * ld_sa, K, av);
+        for (int64_t n = 0; n < N; n++) {
+            const double *bn = bv + n * K;
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; k++) {
+                acc += av[k] * bn[k];
+                mag += fabs(av[k] * bn[k]);
+            }
+            c[m * ldc + n] = acc;
+            if (cabs)
+                cabs[m * ld_cabs + n] = mag;
+        }
+    }
+    free(bv);
     return 0;
 }
