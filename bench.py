@@ -12,7 +12,8 @@ DSL kernel", Performance).  Inputs are resident in HBM before timing.
 
 Prints ONE JSON line.  Extra fields: `roofline` (dominant kernel, HIP-event
 timing on the launch stream), `cpu_baseline` (the CPU oracle on a bounded
-sample of the same workload), `detail` (each op and layout alone, the 3D
+sample of the same workload), `detail` (each op and layout alone, the other
+gated activations, the MX GEMM consumer against the fp8 MFMA peak, the 3D
 expert cast, a copy-kernel ceiling).
 """
 from __future__ import annotations
@@ -348,6 +349,21 @@ def run_detail(inp, fwd_out, bwd_out, stream):
     avg, _ = time_launches(lambda: dst.copy_(inp.w13), 10, 2)
     res["copy_ceiling"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(2 * inp.w13.numel() * 2, avg), 1)}
     del dst
+    torch.cuda.empty_cache()
+    # the consumer: MX GEMM C = A B^T on cast outputs, 16384 x 8192 x 5120
+    # (A the rowwise cast of activations, B of weights); fp8 MFMA roofline
+    gm, gn, gk = 16384, 8192, 5120
+    x = synth.normal_bf16((gm, gk), 1.0, seed=70, device=inp.gate.device)
+    w = synth.normal_bf16((gn, gk), 0.02, seed=71, device=inp.gate.device)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(x, rowwise=True, stream=stream)
+    qb, _, sb, _ = mx.mxfp8_quant_2d(w, rowwise=True, stream=stream)
+    del x, w
+    cg = torch.empty((gm, gn), dtype=torch.float32, device=inp.gate.device)
+    avg, _ = time_launches(lambda: mx.mxfp8_gemm(qa, sa, qb, sb, out=cg, stream=stream), 10, 2)
+    tflops = 2.0 * gm * gn * gk / avg / 1e12
+    res["gemm_16384x8192x5120"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
+                                   "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+    del qa, qb, sa, sb, cg
     torch.cuda.empty_cache()
     # 3D expert cast, 64 experts of 8192 x 5120 (inputs 5.4 GB)
     w = synth.expert_workload(64, device=inp.gate.device)

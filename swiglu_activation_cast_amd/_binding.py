@@ -46,6 +46,7 @@ _SIGNATURES = {
     "mxfp8_quant_2d": [_p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p],
     "mxfp8_quant_3d_colwise": [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p],
     "mxfp8_swiglu_fwd_bf16": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
+    "mxfp8_gemm": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p],
     "mxfp8_swiglu_bwd_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
 }
 
@@ -303,3 +304,35 @@ def gated_act_mxfp8_backward(grad_h: torch.Tensor, gated_input: torch.Tensor, *,
     N = gated_input.shape[1] // 2
     return mxfp8_gated_bwd(grad_h, gated_input[:, :N], gated_input[:, N:], act=activation, rowwise=rowwise,
                            colwise=colwise, out=out, stream=stream)
+
+
+def _u8_matrix(t: torch.Tensor, name: str) -> Tuple[int, int]:
+    if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D uint8 GPU tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    return t.data_ptr(), t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
+
+
+def mxfp8_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor, *,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """C = A B^T (fp32) of MXFP8 operands a [M, K], b [N, K] (uint8 E4M3 codes)
+    with E8M0 scales sa [M, K/32], sb [N, K/32]; K-contiguous, as the casts
+    emit them."""
+    pa, lda = _u8_matrix(a, "a")
+    pb, ldb = _u8_matrix(b, "b")
+    psa, ld_sa = _u8_matrix(sa, "sa")
+    psb, ld_sb = _u8_matrix(sb, "sb")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or tuple(sa.shape) != (M, K // 32) or tuple(sb.shape) != (N, K // 32):
+        raise ValueError("operand shapes do not match a [M, K], sa [M, K/32], b [N, K], sb [N, K/32]")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError(f"out must be a float32 [{M}, {N}] tensor with unit column stride")
+    ldc = out.stride(0) if M > 1 else max(N, 1)
+    st = lib().mxfp8_gemm(pa, lda, psa, ld_sa, pb, ldb, psb, ld_sb, M, N, K, out.data_ptr(), ldc,
+                          _stream(a.device, stream))
+    _check("mxfp8_gemm", st)
+    return out

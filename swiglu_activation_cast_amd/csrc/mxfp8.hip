@@ -13,6 +13,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include "mx_gemm.hpp"
 #include "mx_kernels.hpp"
 #include "mxfp8.h"
 
@@ -332,6 +333,43 @@ mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *ga
   if (st != MXFP8_OK || M == 0 || N == 0) return st;
   Args a = make_args(in, ld, 3, M, N, nullptr, 0, nullptr, 0, nullptr, 0, nullptr, 0);
   return launch_values<mx::OpBwd>(a, dgdu, ld_dgdu, stream);
+}
+
+mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b, int64_t ldb,
+                        const void *sb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc,
+                        void *stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP8_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXFP8_OK;
+  if (!a || !sa || !b || !sb || !c) return MXFP8_ERR_NULL;
+  if (lda < K || ldb < K || lda % 16 != 0 || ldb % 16 != 0 || ld_sa < K / 32 || ld_sb < K / 32 || ldc < N)
+    return MXFP8_ERR_STRIDE;
+  if (!aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3u) != 0) return MXFP8_ERR_ALIGN;
+  if (!extent_ok(M, K, lda) || !extent_ok(N, K, ldb) || !extent_ok(M, K / 32, ld_sa) ||
+      !extent_ok(N, K / 32, ld_sb) || !extent_ok(M, N, ldc))
+    return MXFP8_ERR_OVERFLOW;
+  const int64_t tiles_m = (M + mx::kGT - 1) / mx::kGT, tiles_n = (N + mx::kGT - 1) / mx::kGT;
+  int64_t blocks;
+  if (!mul_ok(tiles_m, tiles_n, &blocks) || blocks > (int64_t)INT32_MAX / 256) return MXFP8_ERR_OVERFLOW;
+  mx::GemmArgs g{};
+  g.a = static_cast<const uint8_t *>(a);
+  g.sa = static_cast<const uint8_t *>(sa);
+  g.b = static_cast<const uint8_t *>(b);
+  g.sb = static_cast<const uint8_t *>(sb);
+  g.lda = lda;
+  g.ld_sa = ld_sa;
+  g.ldb = ldb;
+  g.ld_sb = ld_sb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.c = c;
+  g.ldc = ldc;
+  g.tiles_m = (int32_t)tiles_m;
+  g.tiles_n = (int32_t)tiles_n;
+  void *kargs[] = {&g};
+  hipError_t err = hipLaunchKernel((const void *)&mx::k_mx_gemm, dim3((unsigned)blocks), dim3(256), kargs, 0,
+                                   (hipStream_t)stream);
+  return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
 const char *mxfp8_status_str(mxfp8_status status) {

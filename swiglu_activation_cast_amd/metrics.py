@@ -10,6 +10,7 @@ GB/s x us = these bytes for every row, which the tests check.
 from __future__ import annotations
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak (no sparsity)
 
 
 def _layouts(layout: int) -> int:

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_gated_fwd", "mxfp8_gated_bwd",
                      "mxfp8_quant_2d", "mxfp8_quant_3d_colwise", "mxfp8_swiglu_fwd_bf16", "mxfp8_swiglu_bwd_bf16",
-                     "mxfp8_status_str"}
+                     "mxfp8_gemm", "mxfp8_status_str"}
     for n in names:
         assert getattr(lib, n) is not None
 
@@ -245,3 +245,29 @@ def test_binding_activation_names():
     with pytest.raises(ValueError):
         _act_code("swish")
     assert _act_code("gelu") == 2 and _act_code(3) == 3
+
+
+def gemm(**kw):
+    a = dict(a=A, lda=128, sa=A, ld_sa=4, b=A, ldb=128, sb=A, ld_sb=4, M=64, N=48, K=128, c=A, ldc=48)
+    a.update(kw)
+    return mx.lib().mxfp8_gemm(a["a"], a["lda"], a["sa"], a["ld_sa"], a["b"], a["ldb"], a["sb"], a["ld_sb"], a["M"],
+                               a["N"], a["K"], a["c"], a["ldc"], None)
+
+
+def test_gemm_errors():
+    assert gemm(K=48) == SHAPE                      # partial block
+    assert gemm(M=-1) == SHAPE
+    assert gemm(M=0, a=None, c=None) == OK          # empty result: nothing to do
+    assert gemm(N=0, b=None) == OK
+    assert gemm(a=None) == NULL
+    assert gemm(sb=None) == NULL
+    assert gemm(c=None) == NULL
+    assert gemm(lda=120) == STRIDE                  # < K
+    assert gemm(ldb=136) == STRIDE                  # not a multiple of 16
+    assert gemm(ld_sa=3) == STRIDE
+    assert gemm(ldc=40) == STRIDE
+    assert gemm(a=A + 8) == ALIGN
+    assert gemm(b=A + 4) == ALIGN
+    assert gemm(c=A + 2) == ALIGN
+    assert gemm(sa=A + 1, lda=120) == STRIDE        # scales need no alignment
+    assert gemm(M=1 << 62, K=1 << 20, lda=1 << 20, ldb=1 << 20, ld_sa=1 << 15, ld_sb=1 << 15) == OVERFLOW

@@ -1,0 +1,205 @@
+"""GPU parity of the MX GEMM consumer (mxfp8_gemm) against the oracle.
+
+C = A B^T of MXFP8 operands stored K-contiguous, as the casts emit them
+("[mxfp8 moe training] add compile support", Perf analysis: the cast
+outputs feed a scaled grouped GEMM).
+
+The bar is the error bound of the matrix core's arithmetic.  Every single
+product is exact (checked for all 65536 code pairs), but inside one 64-term
+block-scaled MFMA the products are aligned to the largest one and each is
+truncated toward zero 13 bits below its leading bit (measured: a product
+smaller than 2^-13 of the largest is dropped); the 64-term sum then enters
+the fp32 accumulator.  So, per 64-element K step s with largest product
+magnitude pmax_s:
+    |C_gpu - C| <= sum_s 64 * 2^-13 * pmax_s + (K / 64) * 2^-24 * sum_k |a_k b_k|,
+with C the oracle's exact-product double sum, and NaN exactly where the
+oracle has NaN.
+"""
+import numpy as np
+import pytest
+import torch
+
+import swiglu_activation_cast_amd as mx
+from swiglu_activation_cast_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda", 0)
+
+
+def _rand_operands(rng, rows, K, lo=118, hi=137):
+    codes = rng.integers(0, 256, (rows, K)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A  # no NaN codes
+    return codes, rng.integers(lo, hi, (rows, K // 32)).astype(np.uint8)
+
+
+def _values(q, s):
+    """Element values, decoded independently of the oracle (torch's E4M3 cast)."""
+    v = torch.from_numpy(np.ascontiguousarray(q)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):
+        return v * np.ldexp(1.0, np.repeat(s.astype(np.int64), 32, axis=1) - 127)
+
+
+def _step_max_sum(a, sa, b, sb):
+    """sum over 64-element K steps of the largest |product| in the step."""
+    va, vb = _values(a, sa), _values(b, sb)
+    out = np.zeros((a.shape[0], b.shape[0]))
+    for k0 in range(0, a.shape[1], 64):
+        with np.errstate(invalid="ignore"):
+            p = np.abs(va[:, None, k0:k0 + 64] * vb[None, :, k0:k0 + 64])
+        out += np.nan_to_num(p.max(-1), nan=0.0)
+    return out
+
+
+def _check(oracle_mod, name, a, sa, b, sb, got):
+    want, mag = oracle_mod.mx_gemm(a, sa, b, sb)
+    got = np.asarray(got, np.float64)
+    K = a.shape[1]
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan), f"{name}: NaN pattern differs"
+    bound = 64 * 2.0 ** -13 * _step_max_sum(a, sa, b, sb) + (K / 64 + 1) * 2.0 ** -24 * mag
+    err = np.abs(got[~nan] - want[~nan])
+    worst = (err / np.maximum(bound[~nan], 1e-300)).max(initial=0)
+    assert np.all(err <= bound[~nan]), f"{name}: error {worst:.2f}x the matrix-core bound"
+    print(f"  {name}: worst error {worst:.3f} of the bound")
+    return worst
+
+
+def _to_dev(x, dev):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (37, 45, 96), (128, 128, 64), (200, 130, 256), (256, 384, 1024),
+                                   (64, 300, 4096)])
+def test_gemm_random_codes(oracle_mod, M, N, K):
+    dev = _dev()
+    print(f"case: gemm random codes M={M} N={N} K={K}", flush=True)
+    rng = np.random.default_rng(M * 1000 + N + K)
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, N, K)
+    c = mx.mxfp8_gemm(_to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev))
+    _check(oracle_mod, f"gemm{M}x{N}x{K}", a, sa, b, sb, c.cpu().numpy())
+
+
+def test_gemm_on_cast_outputs(oracle_mod):
+    """The pipeline the casts serve: A = rowwise cast of x [M, K]; B = the
+    colwise cast of w [K, N] (q_col [N, K], s_col [N, K/32]) and, again, the
+    rowwise cast of w^T [N, K]: both layouts give the same B."""
+    dev = _dev()
+    M, N, K = 192, 160, 512
+    x = synth.normal_bf16((M, K), 1.0, seed=50, device=dev)
+    w = synth.normal_bf16((K, N), 0.05, seed=51, device=dev)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(x, rowwise=True, colwise=False)
+    _, qb, _, sbc = mx.mxfp8_quant_2d(w, rowwise=False, colwise=True)
+    qb2, _, sb2, _ = mx.mxfp8_quant_2d(w.t().contiguous(), rowwise=True, colwise=False)
+    assert torch.equal(qb, qb2) and torch.equal(sbc, sb2)
+    c = mx.mxfp8_gemm(qa, sa, qb, sbc)
+    _check(oracle_mod, "cast_pipeline", qa.cpu().numpy(), sa.cpu().numpy(), qb.cpu().numpy(), sbc.cpu().numpy(),
+           c.cpu().numpy())
+    # and the MX result is close to the bf16 product (quantization error only)
+    ref = x.float() @ w.float()
+    rel = ((c - ref).norm() / ref.norm()).item()
+    assert rel < 0.08, rel
+
+
+def test_gemm_nan_blocks(oracle_mod):
+    dev = _dev()
+    rng = np.random.default_rng(7)
+    a, sa = _rand_operands(rng, 64, 128)
+    b, sb = _rand_operands(rng, 64, 128)
+    a[3, 70] = 0x7F
+    sb[10, 2] = 255
+    c = mx.mxfp8_gemm(_to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev))
+    _check(oracle_mod, "nan", a, sa, b, sb, c.cpu().numpy())
+
+
+def test_gemm_strided_and_guarded(oracle_mod):
+    """Operands carved out of wider buffers; C written into a padded buffer
+    whose padding stays untouched."""
+    dev = _dev()
+    rng = np.random.default_rng(8)
+    M, N, K = 70, 90, 160
+    abig, sabig = _rand_operands(rng, M, K + 64)
+    bbig, sbbig = _rand_operands(rng, N, K + 96)
+    a, sa = abig[:, 32:32 + K], sabig[:, 1:1 + K // 32]
+    b, sb = bbig[:, 64:64 + K], sbbig[:, 3:3 + K // 32]
+    da, dsa = _to_dev(abig, dev)[:, 32:32 + K], _to_dev(sabig, dev)[:, 1:1 + K // 32]
+    db, dsb = _to_dev(bbig, dev)[:, 64:64 + K], _to_dev(sbbig, dev)[:, 3:3 + K // 32]
+    big = torch.full((M + 2, N + 7), 7.0, dtype=torch.float32, device=dev)
+    out = big[1:M + 1, 2:N + 2]
+    mx.mxfp8_gemm(da, dsa, db, dsb, out=out)
+    _check(oracle_mod, "strided", a, sa, b, sb, out.cpu().numpy())
+    assert (big[0] == 7).all() and (big[M + 1] == 7).all() and (big[:, :2] == 7).all() and (big[:, N + 2:] == 7).all()
+
+
+def test_gemm_k_zero_gives_zeros():
+    dev = _dev()
+    a = torch.zeros((5, 0), dtype=torch.uint8, device=dev)
+    sa = torch.zeros((5, 0), dtype=torch.uint8, device=dev)
+    b = torch.zeros((3, 0), dtype=torch.uint8, device=dev)
+    sb = torch.zeros((3, 0), dtype=torch.uint8, device=dev)
+    out = torch.full((5, 3), 9.0, device=dev)
+    # K = 0: an empty sum is 0 (tensors of zero width have no data pointer
+    # requirement beyond being non-NULL; allocate 16 bytes to pass one)
+    pad = torch.zeros(16, dtype=torch.uint8, device=dev)
+    st = mx.lib().mxfp8_gemm(pad.data_ptr(), 16, pad.data_ptr(), 1, pad.data_ptr(), 16, pad.data_ptr(), 1,
+                             5, 3, 0, out.data_ptr(), 3, torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert (out == 0).all()
+    del a, sa, b, sb
+
+
+def test_gemm_16384x8192x5120_sampled(oracle_mod):
+    """The bench size: sampled rows and columns against the oracle."""
+    dev = _dev()
+    M, N, K = 16384, 8192, 5120
+    print(f"case: gemm {M}x{N}x{K}, sampled", flush=True)
+    x = synth.normal_bf16((M, K), 1.0, seed=60, device=dev)
+    w = synth.normal_bf16((N, K), 0.02, seed=61, device=dev)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(x, rowwise=True)
+    qb, _, sb, _ = mx.mxfp8_quant_2d(w, rowwise=True)
+    del x, w
+    c = mx.mxfp8_gemm(qa, sa, qb, sb)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 14)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 30)]))
+    ridx = torch.from_numpy(rows).to(dev)
+    cidx = torch.from_numpy(cols).to(dev)
+    got = c[ridx][:, cidx].cpu().numpy()
+    _check(oracle_mod, "bench_size", qa[ridx].cpu().numpy(), sa[ridx].cpu().numpy(), qb[cidx].cpu().numpy(),
+           sb[cidx].cpu().numpy(), got)
+    del qa, qb, sa, sb, c
+    torch.cuda.empty_cache()
+
+
+def test_gemm_single_products_exact_and_truncation_threshold():
+    """The two facts the bound rests on.  With one nonzero per row (K = 32),
+    C[m][n] is one product: exact for all 65536 code pairs, NaN exactly
+    where a code is NaN.  Adding a 1.0 * 1.0 term beside it keeps a product
+    of 2^-13 and drops one just below (the 13-bit truncation)."""
+    dev = _dev()
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    codes = np.arange(256, dtype=np.uint8)
+    a = np.zeros((256, 32), np.uint8)
+    a[:, 0] = codes
+    s = np.full((256, 1), 127, np.uint8)
+    c = mx.mxfp8_gemm(t(a), t(s), t(a), t(s)).cpu().numpy().astype(np.float64)
+    dec = _values(codes.reshape(256, 1).repeat(32, 1), s)[:, 0]
+    want = np.outer(dec, dec)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isnan(c), ~fin)
+    assert np.array_equal(c[fin], want[fin])
+    # two terms: 1.0 plus a small product p in the same MFMA step
+    a2 = a.copy()
+    a2[:, 5] = 0x38
+    c2 = mx.mxfp8_gemm(t(a2), t(s), t(a2), t(s)).cpu().numpy().astype(np.float64)
+    small = fin & (np.abs(want) < 1) & (want > 0)
+    kept = c2[small] - 1.0
+    assert np.all(kept[want[small] >= 2.0 ** -13] == np.trunc(want[small][want[small] >= 2.0 ** -13] * 2 ** 13) / 2 ** 13)
+    assert np.all(kept[want[small] < 2.0 ** -13] == 0)
