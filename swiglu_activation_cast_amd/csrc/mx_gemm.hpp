@@ -36,78 +36,129 @@ struct GemmArgs {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
-constexpr int kGT = 128;   // C tile per workgroup, both dimensions
-constexpr int kGroup = 8;  // tile rows per group in the tile order
+constexpr int kBM = 256, kBN = 256;  // C tile per workgroup
+constexpr int kBK = 64;               // K per LDS stage: one MFMA step
+constexpr int kGroup = 4;             // tile rows per group in the tile order
+constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 128 of C
+constexpr int kStageBytes = kBM * kBK;  // one operand's stage in LDS (bytes)
 
 __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
   return *gptr(reinterpret_cast<const u32x4_t *>(p));
 }
 
-__global__ __launch_bounds__(256) void k_mx_gemm(const GemmArgs g) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 31, h = lane >> 5;
+// LDS position of 16-byte chunk kc (0..3) of tile row `row`: rows of 64
+// bytes, chunks XOR-permuted by (row / 4) % 4, so that the 16 lanes of one
+// quarter-wave reading the same chunk of 16 consecutive rows hit 16
+// different 4-bank groups, and 4 lanes writing one row cover it once.
+__device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 2) & 3u)) << 4); }
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kStageBytes];  // [buffer][A, B]
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
+
   // Tile order: each XCD takes one contiguous range of tiles; inside it,
-  // groups of kGroup tile rows are walked column by column, so the tiles in
-  // flight on one XCD share a few A row-slabs and B column-slabs in its L2.
+  // groups of kGroup tile rows are walked column by column.
   const u32 L = xcd_remap(blockIdx.x, gridDim.x);
   const u32 per_group = (u32)kGroup * (u32)g.tiles_n;
   const u32 grp = L / per_group, in_grp = L % per_group;
   const u32 rows_in_grp = min((u32)kGroup, (u32)g.tiles_m - grp * (u32)kGroup);
-  const int64_t tm = (int64_t)grp * kGroup + in_grp % rows_in_grp, tn = in_grp / rows_in_grp;
-  const int64_t m0 = tm * kGT + (wave >> 1) * 64, n0 = tn * kGT + (wave & 1) * 64;
+  const int64_t m_base = ((int64_t)grp * kGroup + in_grp % rows_in_grp) * kBM;
+  const int64_t n_base = (int64_t)(in_grp / rows_in_grp) * kBN;
 
-  // Operand rows of this lane.  Rows past M (N) are read as row M-1 (N-1):
-  // in bounds, and their results are never stored.
-  const uint8_t *arow[2], *brow[2], *sarow[2], *sbrow[2];
-#pragma unroll
-  for (int i = 0; i < 2; i++) {
-    const int64_t m = min(m0 + 32 * i + r, g.M - 1), n = min(n0 + 32 * i + r, g.N - 1);
-    arow[i] = g.a + m * g.lda + 16 * h;
-    sarow[i] = g.sa + m * g.ld_sa + h;
-    brow[i] = g.b + n * g.ldb + 16 * h;
-    sbrow[i] = g.sb + n * g.ld_sb + h;
-  }
+  // ---- global -> LDS assignment: thread t moves chunk t % 4 of tile rows
+  // t / 4 + 64 j (j = 0..3) of A and of B.  Rows past M (N) are read as the
+  // last row: in bounds, never stored.
+  const uint8_t *a_tile = g.a + m_base * g.lda, *b_tile = g.b + n_base * g.ldb;  // uniform
+  const u32 ld_row = (u32)t >> 2, ld_kc = (u32)t & 3u;
+  const u32 a_rows = (u32)min<int64_t>(g.M - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
 
-  v16f_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = v16f_t{};
-
+  // ---- scales: lane r + 32 h carries the scale of block h of the step for
+  // its row of each 32-row tile
+  const uint8_t *sa_tile = g.sa + m_base * g.ld_sa, *sb_tile = g.sb + n_base * g.ld_sb;  // uniform
   const int64_t nblk = g.K / 32;
-  for (int64_t k0 = 0; k0 < g.K; k0 += 64) {
-    const int64_t b0 = k0 / 32;
-    const bool second = b0 + 1 < nblk;  // uniform: the MFMA's second block exists
-    v8i_t av[2], bv[2];
-    int as[2], bs[2];
+  const int nstage = (int)((g.K + kBK - 1) / kBK);
+
+  u32x4_t sta[4], stb[4];  // the next stage, global -> registers -> LDS
+  int nsa[4], nsb[4];      // its scale bytes per 32-row tile
+  auto load_stage = [&](int st) {
+    const int64_t k0 = (int64_t)st * kBK;
+    const bool kc_ok = k0 + 16 * (int64_t)ld_kc < g.K;  // whole 16-byte chunks (K % 32 == 0)
 #pragma unroll
-    for (int i = 0; i < 2; i++) {
-      const u32x4_t alo = gload16(arow[i] + k0);
-      const u32x4_t ahi = second ? gload16(arow[i] + k0 + 32) : u32x4_t{0, 0, 0, 0};
-      av[i] = v8i_t{(int)alo.x, (int)alo.y, (int)alo.z, (int)alo.w, (int)ahi.x, (int)ahi.y, (int)ahi.z, (int)ahi.w};
-      const u32x4_t blo = gload16(brow[i] + k0);
-      const u32x4_t bhi = second ? gload16(brow[i] + k0 + 32) : u32x4_t{0, 0, 0, 0};
-      bv[i] = v8i_t{(int)blo.x, (int)blo.y, (int)blo.z, (int)blo.w, (int)bhi.x, (int)bhi.y, (int)bhi.z, (int)bhi.w};
-      // lane m + 32 h carries the scale of block b0 + h; a missing second
-      // block (K % 64 == 32) has zero data and takes scale 2^0
-      as[i] = (h == 0 || second) ? (int)*gptr(sarow[i] + b0) : 127;
-      bs[i] = (h == 0 || second) ? (int)*gptr(sbrow[i] + b0) : 127;
+    for (int j = 0; j < 4; j++) {
+      const u32 ra = min(ld_row + 64u * j, a_rows - 1), rb = min(ld_row + 64u * j, b_rows - 1);
+      sta[j] = kc_ok ? gload16(byte_off(a_tile + k0, ra * (u32)g.lda + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
+      stb[j] = kc_ok ? gload16(byte_off(b_tile + k0, rb * (u32)g.ldb + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
+    }
+    const int64_t kb = k0 / 32;  // + h below
+    const bool ok = kb + h < nblk;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const u32 ra = min((u32)(wm * 128 + 32 * i + r), a_rows - 1), rb = min((u32)(wn * 128 + 32 * i + r), b_rows - 1);
+      nsa[i] = ok ? (int)*gptr(byte_off(sa_tile + kb, ra * (u32)g.ld_sa + (u32)h)) : 127;
+      nsb[i] = ok ? (int)*gptr(byte_off(sb_tile + kb, rb * (u32)g.ld_sb + (u32)h)) : 127;
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const u32 o = lds_off(ld_row + 64u * j, ld_kc);
+      *reinterpret_cast<u32x4_t *>(&smem[buf][0][o]) = sta[j];
+      *reinterpret_cast<u32x4_t *>(&smem[buf][1][o]) = stb[j];
+    }
+  };
+
+  v16f_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) acc[i][j] = v16f_t{};
+
+  int csa[4], csb[4];
+  load_stage(0);
+  store_stage(0);
+#pragma unroll
+  for (int i = 0; i < 4; i++) csa[i] = nsa[i], csb[i] = nsb[i];
+  __syncthreads();
+
+  for (int st = 0; st < nstage; st++) {
+    const int buf = st & 1;
+    const bool more = st + 1 < nstage;  // uniform
+    if (more) load_stage(st + 1);
+    v8i_t bv[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const u32 row = (u32)(wn * 128 + 32 * j + r);
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smem[buf][1][lds_off(row, (u32)h)]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smem[buf][1][lds_off(row, 2u + h)]);
+      bv[j] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < 4; i++) {
+      const u32 row = (u32)(wm * 128 + 32 * i + r);
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smem[buf][0][lds_off(row, (u32)h)]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smem[buf][0][lds_off(row, 2u + h)]);
+      const v8i_t av = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-      for (int j = 0; j < 2; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[i], bv[j], acc[i][j], 0, 0, 0, as[i], 0, bs[j]);
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], 0, 0, 0, csa[i], 0, csb[j]);
+    }
+    if (more) {
+      store_stage(buf ^ 1);
+#pragma unroll
+      for (int i = 0; i < 4; i++) csa[i] = nsa[i], csb[i] = nsb[i];
+    }
+    __syncthreads();
   }
 
 #pragma unroll
-  for (int i = 0; i < 2; i++)
+  for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int64_t col = n0 + 32 * j + r;
+    for (int j = 0; j < 4; j++) {
+      const int64_t col = n_base + wn * 128 + 32 * j + r;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        const int64_t row = m0 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
+        const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
         if (row < g.M && col < g.N) *gptr(g.c + row * g.ldc + col) = acc[i][j][v];
       }
     }

@@ -347,9 +347,13 @@ mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_s
   if (!extent_ok(M, K, lda) || !extent_ok(N, K, ldb) || !extent_ok(M, K / 32, ld_sa) ||
       !extent_ok(N, K / 32, ld_sb) || !extent_ok(M, N, ldc))
     return MXFP8_ERR_OVERFLOW;
-  const int64_t tiles_m = (M + mx::kGT - 1) / mx::kGT, tiles_n = (N + mx::kGT - 1) / mx::kGT;
+  // tile-relative offsets are 32-bit: 256 rows of either operand must span less than 2^32 bytes
+  if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || ld_sa >= (int64_t(1) << 23) ||
+      ld_sb >= (int64_t(1) << 23))
+    return MXFP8_ERR_OVERFLOW;
+  const int64_t tiles_m = (M + mx::kBM - 1) / mx::kBM, tiles_n = (N + mx::kBN - 1) / mx::kBN;
   int64_t blocks;
-  if (!mul_ok(tiles_m, tiles_n, &blocks) || blocks > (int64_t)INT32_MAX / 256) return MXFP8_ERR_OVERFLOW;
+  if (!mul_ok(tiles_m, tiles_n, &blocks) || blocks > (int64_t)INT32_MAX / mx::kGemmThreads) return MXFP8_ERR_OVERFLOW;
   mx::GemmArgs g{};
   g.a = static_cast<const uint8_t *>(a);
   g.sa = static_cast<const uint8_t *>(sa);
@@ -367,8 +371,8 @@ mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_s
   g.tiles_m = (int32_t)tiles_m;
   g.tiles_n = (int32_t)tiles_n;
   void *kargs[] = {&g};
-  hipError_t err = hipLaunchKernel((const void *)&mx::k_mx_gemm, dim3((unsigned)blocks), dim3(256), kargs, 0,
-                                   (hipStream_t)stream);
+  hipError_t err = hipLaunchKernel((const void *)&mx::k_mx_gemm, dim3((unsigned)blocks), dim3(mx::kGemmThreads),
+                                   kargs, 0, (hipStream_t)stream);
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
 
