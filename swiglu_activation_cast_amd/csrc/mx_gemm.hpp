@@ -36,11 +36,11 @@ struct GemmArgs {
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256, kBN = 256;  // C tile per workgroup
+constexpr int kBM = 256, kBN = 128;  // C tile per workgroup
 constexpr int kBK = 64;               // K per LDS stage: one MFMA step
 constexpr int kGroup = 4;             // tile rows per group in the tile order
-constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 128 of C
-constexpr int kStageBytes = kBM * kBK;  // one operand's stage in LDS (bytes)
+constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 64 of C
+constexpr int kStageA = kBM * kBK, kStageB = kBN * kBK;  // one stage of each operand in LDS (bytes)
 
 __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
   return *gptr(reinterpret_cast<const u32x4_t *>(p));
@@ -52,8 +52,8 @@ __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
 // different 4-bank groups, and 4 lanes writing one row cover it once.
 __device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 2) & 3u)) << 4); }
 
-__global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kStageBytes];  // [buffer][A, B]
+__global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t smemA[2][kStageA], smemB[2][kStageB];  // [buffer]
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
 
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   const int64_t n_base = (int64_t)(in_grp / rows_in_grp) * kBN;
 
   // ---- global -> LDS assignment: thread t moves chunk t % 4 of tile rows
-  // t / 4 + 64 j (j = 0..3) of A and of B.  Rows past M (N) are read as the
+  // t / 4 + 64 j of A (j = 0..3) and of B (j = 0..1).  Rows past M (N) are read as the
   // last row: in bounds, never stored.
   const uint8_t *a_tile = g.a + m_base * g.lda, *b_tile = g.b + n_base * g.ldb;  // uniform
   const u32 ld_row = (u32)t >> 2, ld_kc = (u32)t & 3u;
@@ -79,74 +79,84 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   const int64_t nblk = g.K / 32;
   const int nstage = (int)((g.K + kBK - 1) / kBK);
 
-  u32x4_t sta[4], stb[4];  // the next stage, global -> registers -> LDS
-  int nsa[4], nsb[4];      // its scale bytes per 32-row tile
+  u32x4_t sta[4], stb[2];  // the next stage, global -> registers -> LDS
+  int nsa[4], nsb[2];      // its scale bytes per 32-row tile
   auto load_stage = [&](int st) {
     const int64_t k0 = (int64_t)st * kBK;
     const bool kc_ok = k0 + 16 * (int64_t)ld_kc < g.K;  // whole 16-byte chunks (K % 32 == 0)
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      const u32 ra = min(ld_row + 64u * j, a_rows - 1), rb = min(ld_row + 64u * j, b_rows - 1);
+      const u32 ra = min(ld_row + 64u * j, a_rows - 1);
       sta[j] = kc_ok ? gload16(byte_off(a_tile + k0, ra * (u32)g.lda + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const u32 rb = min(ld_row + 64u * j, b_rows - 1);
       stb[j] = kc_ok ? gload16(byte_off(b_tile + k0, rb * (u32)g.ldb + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
     }
     const int64_t kb = k0 / 32;  // + h below
     const bool ok = kb + h < nblk;
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      const u32 ra = min((u32)(wm * 128 + 32 * i + r), a_rows - 1), rb = min((u32)(wn * 128 + 32 * i + r), b_rows - 1);
+      const u32 ra = min((u32)(wm * 128 + 32 * i + r), a_rows - 1);
       nsa[i] = ok ? (int)*gptr(byte_off(sa_tile + kb, ra * (u32)g.ld_sa + (u32)h)) : 127;
-      nsb[i] = ok ? (int)*gptr(byte_off(sb_tile + kb, rb * (u32)g.ld_sb + (u32)h)) : 127;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const u32 rb = min((u32)(wn * 64 + 32 * j + r), b_rows - 1);
+      nsb[j] = ok ? (int)*gptr(byte_off(sb_tile + kb, rb * (u32)g.ld_sb + (u32)h)) : 127;
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const u32 o = lds_off(ld_row + 64u * j, ld_kc);
-      *reinterpret_cast<u32x4_t *>(&smem[buf][0][o]) = sta[j];
-      *reinterpret_cast<u32x4_t *>(&smem[buf][1][o]) = stb[j];
-    }
+    for (int j = 0; j < 4; j++) *reinterpret_cast<u32x4_t *>(&smemA[buf][lds_off(ld_row + 64u * j, ld_kc)]) = sta[j];
+#pragma unroll
+    for (int j = 0; j < 2; j++) *reinterpret_cast<u32x4_t *>(&smemB[buf][lds_off(ld_row + 64u * j, ld_kc)]) = stb[j];
   };
 
-  v16f_t acc[4][4];
+  v16f_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = v16f_t{};
+    for (int j = 0; j < 2; j++) acc[i][j] = v16f_t{};
 
-  int csa[4], csb[4];
+  int csa[4], csb[2];
   load_stage(0);
   store_stage(0);
 #pragma unroll
-  for (int i = 0; i < 4; i++) csa[i] = nsa[i], csb[i] = nsb[i];
+  for (int i = 0; i < 4; i++) csa[i] = nsa[i];
+#pragma unroll
+  for (int j = 0; j < 2; j++) csb[j] = nsb[j];
   __syncthreads();
 
   for (int st = 0; st < nstage; st++) {
     const int buf = st & 1;
     const bool more = st + 1 < nstage;  // uniform
     if (more) load_stage(st + 1);
-    v8i_t bv[4];
+    v8i_t bv[2];
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const u32 row = (u32)(wn * 128 + 32 * j + r);
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smem[buf][1][lds_off(row, (u32)h)]);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smem[buf][1][lds_off(row, 2u + h)]);
+    for (int j = 0; j < 2; j++) {
+      const u32 row = (u32)(wn * 64 + 32 * j + r);
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smemB[buf][lds_off(row, (u32)h)]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smemB[buf][lds_off(row, 2u + h)]);
       bv[j] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const u32 row = (u32)(wm * 128 + 32 * i + r);
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smem[buf][0][lds_off(row, (u32)h)]);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smem[buf][0][lds_off(row, 2u + h)]);
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smemA[buf][lds_off(row, (u32)h)]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smemA[buf][lds_off(row, 2u + h)]);
       const v8i_t av = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < 2; j++)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], 0, 0, 0, csa[i], 0, csb[j]);
     }
     if (more) {
       store_stage(buf ^ 1);
 #pragma unroll
-      for (int i = 0; i < 4; i++) csa[i] = nsa[i], csb[i] = nsb[i];
+      for (int i = 0; i < 4; i++) csa[i] = nsa[i];
+#pragma unroll
+      for (int j = 0; j < 2; j++) csb[j] = nsb[j];
     }
     __syncthreads();
   }
@@ -154,8 +164,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t col = n_base + wn * 128 + 32 * j + r;
+    for (int j = 0; j < 2; j++) {
+      const int64_t col = n_base + wn * 64 + 32 * j + r;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
