@@ -70,6 +70,8 @@ def _load():
         "orc_swiglu_bwd": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, ctypes.c_int] + [_p, _i64] * 4),
         "orc_quant_3d_colwise": (ctypes.c_int, [_p, _i64, _i64, _i64, _i64, _i64, _p, _p]),
         "orc_mx_gemm": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64]),
+        "orc_mx_grouped_gemm": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64,
+                                               _i64, _p, _i64, _p, _i64]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -311,4 +313,25 @@ def mx_gemm(a, sa, b, sb):
     cabs = np.zeros((M, N), np.float64)
     _check(_load().orc_mx_gemm(_ptr(a), lda, _ptr(sa), ld_sa, _ptr(b), ldb, _ptr(sb), ld_sb, M, N, K,
                                _ptr(c), N, _ptr(cabs), N), "mx_gemm")
+    return c, cabs
+
+
+def mx_grouped_gemm(a, sa, b, sb, offsets):
+    """Grouped C = A B_g^T: rows of a [M, K] split by the cumulative end
+    offsets (int32, length G) into groups, group g against b[g] [N, K] with
+    scales sb[g] [N, K/32].  Returns (C, sum |products|) as float64 [M, N];
+    rows no group covers are NaN (never written)."""
+    a, lda = _u8_mat(a)
+    sa, ld_sa = _u8_mat(sa)
+    b = np.ascontiguousarray(np.asarray(b, np.uint8))
+    sb = np.ascontiguousarray(np.asarray(sb, np.uint8))
+    offs = np.ascontiguousarray(np.asarray(offsets, np.int32))
+    M, K = a.shape
+    G, N, Kb = b.shape
+    assert Kb == K and sb.shape == (G, N, K // 32) and offs.shape == (G,)
+    c = np.full((M, N), np.nan)
+    cabs = np.full((M, N), np.nan)
+    _check(_load().orc_mx_grouped_gemm(_ptr(a), lda, _ptr(sa), ld_sa, _ptr(b), K, N * K, _ptr(sb), K // 32,
+                                       N * (K // 32), _ptr(offs), G, M, N, K, _ptr(c), N, _ptr(cabs), N),
+           "mx_grouped_gemm")
     return c, cabs

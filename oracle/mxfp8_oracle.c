@@ -505,3 +505,35 @@ int orc_mx_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa,
     free(bv);
     return 0;
 }
+
+/* Grouped (2D x 3D) form of the consumer, as a mixture-of-experts layer runs
+ * it [P4, Perf analysis: M=16640, G=4, N=8192, K=5120 grouped GEMMs]: the
+ * rows of A are split into G consecutive groups by the cumulative end
+ * offsets offs[0..G-1] (group g is rows [offs[g-1], offs[g]), offs[-1] = 0),
+ * and group g multiplies expert g's operand b + g*stride_b [N, K] (scales
+ * sb + g*stride_sb [N, K/32]).  Offsets are clamped so that groups stay
+ * ordered and inside [0, M]: end_g = min(max(offs[g], start_g), M).  Rows
+ * at or past the last group's end are not written. */
+int orc_mx_grouped_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa,
+                        const uint8_t *b, int64_t ldb, int64_t stride_b, const uint8_t *sb, int64_t ld_sb,
+                        int64_t stride_sb, const int32_t *offs, int64_t G, int64_t M, int64_t N, int64_t K,
+                        double *c, int64_t ldc, double *cabs, int64_t ld_cabs)
+{
+    if (G < 0 || M < 0 || N < 0 || K < 0 || K % 32 != 0)
+        return -1;
+    int64_t start = 0;
+    for (int64_t g = 0; g < G; g++) {
+        int64_t end = offs[g];
+        if (end < start)
+            end = start;
+        if (end > M)
+            end = M;
+        int rc = orc_mx_gemm(a + start * lda, lda, sa + start * ld_sa, ld_sa, b + g * stride_b, ldb,
+                             sb + g * stride_sb, ld_sb, end - start, N, K, c + start * ldc, ldc,
+                             cabs ? cabs + start * ld_cabs : NULL, ld_cabs);
+        if (rc != 0)
+            return rc;
+        start = end;
+    }
+    return 0;
+}

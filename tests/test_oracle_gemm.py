@@ -103,3 +103,40 @@ def test_rejects_partial_blocks(oracle_mod):
         c = np.zeros((1, 1))
         oracle_mod._check(oracle_mod.lib().orc_mx_gemm(0, 40, 0, 1, 0, 40, 0, 1, 1, 1, 40, c.ctypes.data, 1, 0, 1),
                           "mx_gemm")
+
+
+def test_grouped_matches_independent_per_group_products(oracle_mod):
+    """Grouped form: each group's rows against its own expert, checked with
+    the independent decode; an empty group, and rows past the last offset
+    left unwritten."""
+    rng = np.random.default_rng(6)
+    M, N, K, G = 90, 20, 96, 4
+    a, sa = _rand_operands(rng, M, K)
+    bs = [_rand_operands(rng, N, K) for _ in range(G)]
+    b = np.stack([x[0] for x in bs])
+    sb = np.stack([x[1] for x in bs])
+    offs = np.array([17, 17, 60, 81], np.int32)  # group 1 empty; rows 81.. uncovered
+    c, cabs = oracle_mod.mx_grouped_gemm(a, sa, b, sb, offs)
+    da = _dequant_torch(a, sa)
+    start = 0
+    for g in range(G):
+        end = offs[g]
+        ref = da[start:end] @ _dequant_torch(b[g], sb[g]).T
+        assert np.all(np.abs(c[start:end] - ref) <= 1e-13 * cabs[start:end])
+        start = end
+    assert np.isnan(c[81:]).all()
+
+
+def test_grouped_offsets_are_clamped(oracle_mod):
+    """Decreasing or too-large offsets are clamped into ordered groups
+    within [0, M]: no row is read or written outside A and C."""
+    rng = np.random.default_rng(7)
+    M, N, K = 40, 8, 64
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, 3 * N, K)
+    b, sb = b.reshape(3, N, K), sb.reshape(3, N, K // 32)
+    c, _ = oracle_mod.mx_grouped_gemm(a, sa, b, sb, np.array([25, 10, 1000], np.int32))
+    # groups: [0, 25) expert 0, [25, 25) expert 1 (clamped up), [25, 40) expert 2 (clamped down)
+    c0, _ = oracle_mod.mx_gemm(a[:25], sa[:25], b[0], sb[0])
+    c2, _ = oracle_mod.mx_gemm(a[25:], sa[25:], b[2], sb[2])
+    assert np.array_equal(c[:25], c0) and np.array_equal(c[25:], c2)
