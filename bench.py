@@ -365,6 +365,23 @@ def run_detail(inp, fwd_out, bwd_out, stream):
                                    "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
     del qa, qb, sa, sb, cg
     torch.cuda.empty_cache()
+    # grouped form at the pages' shape: 16640 tokens over 4 experts of 8192 x
+    # 5120 ("[mxfp8 moe training] add compile support", Perf analysis)
+    gm, gn, gk, ng = 16640, 8192, 5120, 4
+    x = synth.normal_bf16((gm, gk), 1.0, seed=72, device=inp.gate.device)
+    w = synth.normal_bf16((ng * gn, gk), 0.02, seed=73, device=inp.gate.device)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(x, rowwise=True, stream=stream)
+    qb, _, sb, _ = mx.mxfp8_quant_2d(w, rowwise=True, stream=stream)
+    del x, w
+    offs = torch.arange(1, ng + 1, dtype=torch.int32, device=inp.gate.device) * (gm // ng)
+    cg = torch.empty((gm, gn), dtype=torch.float32, device=inp.gate.device)
+    qb3, sb3 = qb.view(ng, gn, gk), sb.view(ng, gn, gk // 32)
+    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm(qa, sa, qb3, sb3, offs, out=cg, stream=stream), 10, 2)
+    tflops = 2.0 * gm * gn * gk / avg / 1e12
+    res["grouped_gemm_16640x8192x5120_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
+                                              "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+    del qa, qb, sa, sb, qb3, sb3, cg, offs
+    torch.cuda.empty_cache()
     # 3D expert cast, 64 experts of 8192 x 5120 (inputs 5.4 GB)
     w = synth.expert_workload(64, device=inp.gate.device)
     q = torch.empty((64, 5120, 8192), dtype=torch.uint8, device=w.device)

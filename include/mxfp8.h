@@ -210,6 +210,31 @@ mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_s
                         const void *b, int64_t ldb, const void *sb, int64_t ld_sb,
                         int64_t M, int64_t N, int64_t K, float *c, int64_t ldc, void *stream);
 
+/*
+ * Grouped (2D x 3D) form of mxfp8_gemm, as a mixture-of-experts layer runs
+ * it: "[mxfp8 moe training] add compile support", Perf analysis (grouped
+ * GEMMs at M=16640, G=4, N=8192, K=5120) and Summary (size buffers by an
+ * upper bound instead of reading the last offset back to the host).
+ *   a, sa     : as in mxfp8_gemm, [M, K] and [M, K/32]
+ *   b, sb     : G experts; expert g is b + g * stride_b [N, K] (row stride
+ *               ldb) with scales sb + g * stride_sb [N, K/32] (ld_sb);
+ *               stride_b a multiple of 16 and >= (N-1)*ldb + K
+ *   offsets   : DEVICE int32 [G], cumulative end rows: group g is rows
+ *               [offsets[g-1], offsets[g]) of A and C (offsets[-1] = 0)
+ *   c         : fp32 [M, N]; rows of group g get A_g B_g^T
+ * The offsets are read on the GPU only; the launch covers M/256 + G row
+ * tiles, an upper bound.  They are clamped into ordered groups inside
+ * [0, M] (end_g = min(max(offsets[g], end_{g-1}), M)), so malformed
+ * offsets cannot cause out-of-range accesses; rows past the last group's
+ * end are not written.  1 <= G <= 1024; G == 0 returns MXFP8_OK and
+ * launches nothing.  Same numerics as mxfp8_gemm.
+ */
+mxfp8_status mxfp8_grouped_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa,
+                                const void *b, int64_t ldb, int64_t stride_b,
+                                const void *sb, int64_t ld_sb, int64_t stride_sb,
+                                const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K,
+                                float *c, int64_t ldc, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *mxfp8_status_str(mxfp8_status status);
 

@@ -47,6 +47,8 @@ _SIGNATURES = {
     "mxfp8_quant_3d_colwise": [_p, _i64, _i64, _i64, _i64, _i64, _p, _p, _p],
     "mxfp8_swiglu_fwd_bf16": [_p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
     "mxfp8_gemm": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p],
+    "mxfp8_grouped_gemm": [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64,
+                           _p],
     "mxfp8_swiglu_bwd_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
 }
 
@@ -335,4 +337,39 @@ def mxfp8_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Ten
     st = lib().mxfp8_gemm(pa, lda, psa, ld_sa, pb, ldb, psb, ld_sb, M, N, K, out.data_ptr(), ldc,
                           _stream(a.device, stream))
     _check("mxfp8_gemm", st)
+    return out
+
+
+def mxfp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                       offsets: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Grouped C = A B_g^T (fp32): rows of a [M, K] split into groups by the
+    cumulative end offsets (int32 GPU tensor [G]); group g against b[g]
+    [N, K] with scales sb[g] [N, K/32].  Rows past the last offset are left
+    as they are in `out` (uninitialized when `out` is None)."""
+    pa, lda = _u8_matrix(a, "a")
+    psa, ld_sa = _u8_matrix(sa, "sa")
+    if b.dtype != torch.uint8 or not b.is_cuda or b.dim() != 3 or sb.dtype != torch.uint8 or sb.dim() != 3:
+        raise ValueError("b and sb must be 3-D uint8 GPU tensors [G, N, K] and [G, N, K/32]")
+    if b.stride(2) != 1 or sb.stride(2) != 1:
+        raise ValueError("b and sb must have unit stride along K")
+    if offsets.dtype != torch.int32 or not offsets.is_cuda or offsets.dim() != 1:
+        raise ValueError("offsets must be a 1-D int32 GPU tensor")
+    M, K = a.shape
+    G, N, _ = b.shape
+    if tuple(b.shape) != (G, N, K) or tuple(sb.shape) != (G, N, K // 32) or tuple(sa.shape) != (M, K // 32):
+        raise ValueError("shapes must be a [M, K], sa [M, K/32], b [G, N, K], sb [G, N, K/32]")
+    if offsets.shape[0] != G or (G > 1 and offsets.stride(0) != 1):
+        raise ValueError("offsets must hold G contiguous entries")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    elif out.dtype != torch.float32 or tuple(out.shape) != (M, N) or (N > 1 and out.stride(1) != 1):
+        raise ValueError(f"out must be a float32 [{M}, {N}] tensor with unit column stride")
+    ldb = b.stride(1) if N > 1 else K
+    ld_sb = sb.stride(1) if N > 1 else K // 32
+    stride_b = b.stride(0) if G > 1 else N * ldb
+    stride_sb = sb.stride(0) if G > 1 else N * ld_sb
+    ldc = out.stride(0) if M > 1 else max(N, 1)
+    st = lib().mxfp8_grouped_gemm(pa, lda, psa, ld_sa, b.data_ptr(), ldb, stride_b, sb.data_ptr(), ld_sb, stride_sb,
+                                  offsets.data_ptr(), G, M, N, K, out.data_ptr(), ldc, _stream(a.device, stream))
+    _check("mxfp8_grouped_gemm", st)
     return out

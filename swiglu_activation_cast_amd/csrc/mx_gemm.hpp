@@ -30,8 +30,15 @@ struct GemmArgs {
   int64_t M, N, K;
   float *c;
   int64_t ldc;
-  int32_t tiles_m, tiles_n;
+  int32_t tiles_m, tiles_n;  // tiles_m: an upper bound in the grouped form
+  // grouped form: G groups of rows by cumulative end offsets (device
+  // memory), group g against b + g * stride_b, sb + g * stride_sb
+  const int32_t *offs;
+  int32_t G;
+  int64_t stride_b, stride_sb;
 };
+
+constexpr int kMaxGroups = 1024;
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
@@ -52,6 +59,7 @@ __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
 // different 4-bank groups, and 4 lanes writing one row cover it once.
 __device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 2) & 3u)) << 4); }
 
+template <bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smemA[2][kStageA], smemB[2][kStageB];  // [buffer]
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -63,19 +71,48 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
   const u32 per_group = (u32)kGroup * (u32)g.tiles_n;
   const u32 grp = L / per_group, in_grp = L % per_group;
   const u32 rows_in_grp = min((u32)kGroup, (u32)g.tiles_m - grp * (u32)kGroup);
-  const int64_t m_base = ((int64_t)grp * kGroup + in_grp % rows_in_grp) * kBM;
+  const int64_t tm = (int64_t)grp * kGroup + in_grp % rows_in_grp;
   const int64_t n_base = (int64_t)(in_grp / rows_in_grp) * kBN;
+
+  // Rows of this tile: [m_base, m_end).  In the grouped form tile row tm is
+  // the (tm - tiles before)-th tile of the group it falls in, counting each
+  // group's tiles from its own first row; the grid holds an upper bound of
+  // tiles (rows / 256 + groups), and tiles past the real count do nothing.
+  int64_t m_base = tm * kBM, m_end = g.M;
+  const uint8_t *b_mat = g.b, *sb_mat = g.sb;
+  if constexpr (GROUPED) {
+    __shared__ int32_t offs_s[kMaxGroups];
+    for (int e = t; e < g.G; e += kGemmThreads) offs_s[e] = g.offs[e];
+    __syncthreads();
+    int64_t start = 0, before = 0;
+    int e_hit = -1;
+    for (int e = 0; e < g.G; e++) {  // uniform: every lane walks the same offsets
+      const int64_t end = min<int64_t>(max<int64_t>((int64_t)offs_s[e], start), g.M);
+      const int64_t nt = (end - start + kBM - 1) / kBM;
+      if (tm < before + nt) {
+        e_hit = e;
+        m_base = start + (tm - before) * kBM;
+        m_end = end;
+        break;
+      }
+      before += nt;
+      start = end;
+    }
+    if (e_hit < 0) return;  // uniform over the workgroup: past the real tiles
+    b_mat = g.b + (int64_t)e_hit * g.stride_b;
+    sb_mat = g.sb + (int64_t)e_hit * g.stride_sb;
+  }
 
   // ---- global -> LDS assignment: thread t moves chunk t % 4 of tile rows
   // t / 4 + 64 j of A (j = 0..3) and of B (j = 0..1).  Rows past M (N) are read as the
   // last row: in bounds, never stored.
-  const uint8_t *a_tile = g.a + m_base * g.lda, *b_tile = g.b + n_base * g.ldb;  // uniform
+  const uint8_t *a_tile = g.a + m_base * g.lda, *b_tile = b_mat + n_base * g.ldb;  // uniform
   const u32 ld_row = (u32)t >> 2, ld_kc = (u32)t & 3u;
-  const u32 a_rows = (u32)min<int64_t>(g.M - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
+  const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
 
   // ---- scales: lane r + 32 h carries the scale of block h of the step for
   // its row of each 32-row tile
-  const uint8_t *sa_tile = g.sa + m_base * g.ld_sa, *sb_tile = g.sb + n_base * g.ld_sb;  // uniform
+  const uint8_t *sa_tile = g.sa + m_base * g.ld_sa, *sb_tile = sb_mat + n_base * g.ld_sb;  // uniform
   const int64_t nblk = g.K / 32;
   const int nstage = (int)((g.K + kBK - 1) / kBK);
 
@@ -169,7 +206,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
-        if (row < g.M && col < g.N) *gptr(g.c + row * g.ldc + col) = acc[i][j][v];
+        if (row < m_end && col < g.N) *gptr(g.c + row * g.ldc + col) = acc[i][j][v];
       }
     }
 }

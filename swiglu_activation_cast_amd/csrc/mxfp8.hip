@@ -335,23 +335,45 @@ mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *ga
   return launch_values<mx::OpBwd>(a, dgdu, ld_dgdu, stream);
 }
 
-mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b, int64_t ldb,
-                        const void *sb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc,
-                        void *stream) {
-  if (M < 0 || N < 0 || K < 0 || K % 32 != 0) return MXFP8_ERR_SHAPE;
+}  // extern "C"
+
+namespace {
+
+// Checks and launch shared by the plain and grouped GEMM.  G == 0 is the
+// plain form (offsets unused, one expert).
+mxfp8_status gemm_launch(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b, int64_t ldb,
+                         int64_t stride_b, const void *sb, int64_t ld_sb, int64_t stride_sb, const int32_t *offs,
+                         int64_t G, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc, void *stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || G < 0 || G > mx::kMaxGroups) return MXFP8_ERR_SHAPE;
   if (M == 0 || N == 0) return MXFP8_OK;
-  if (!a || !sa || !b || !sb || !c) return MXFP8_ERR_NULL;
+  if (!a || !sa || !b || !sb || !c || (G > 0 && !offs)) return MXFP8_ERR_NULL;
   if (lda < K || ldb < K || lda % 16 != 0 || ldb % 16 != 0 || ld_sa < K / 32 || ld_sb < K / 32 || ldc < N)
     return MXFP8_ERR_STRIDE;
-  if (!aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3u) != 0) return MXFP8_ERR_ALIGN;
+  if (G > 0) {
+    int64_t span_b, span_sb;
+    if (!mul_ok(N - 1, ldb, &span_b) || !add_ok(span_b, K, &span_b) || !mul_ok(N - 1, ld_sb, &span_sb) ||
+        !add_ok(span_sb, K / 32, &span_sb))
+      return MXFP8_ERR_OVERFLOW;
+    if (stride_b < span_b || stride_b % 16 != 0 || stride_sb < span_sb) return MXFP8_ERR_STRIDE;
+  }
+  if (!aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3u) != 0 || ((uintptr_t)offs & 3u) != 0)
+    return MXFP8_ERR_ALIGN;
   if (!extent_ok(M, K, lda) || !extent_ok(N, K, ldb) || !extent_ok(M, K / 32, ld_sa) ||
       !extent_ok(N, K / 32, ld_sb) || !extent_ok(M, N, ldc))
     return MXFP8_ERR_OVERFLOW;
+  if (G > 0) {
+    int64_t e;
+    if (!mul_ok(G - 1, stride_b, &e) || e >= (INT64_MAX >> 2) || !mul_ok(G - 1, stride_sb, &e) ||
+        e >= (INT64_MAX >> 2))
+      return MXFP8_ERR_OVERFLOW;
+  }
   // tile-relative offsets are 32-bit: 256 rows of either operand must span less than 2^32 bytes
   if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || ld_sa >= (int64_t(1) << 23) ||
       ld_sb >= (int64_t(1) << 23))
     return MXFP8_ERR_OVERFLOW;
-  const int64_t tiles_m = (M + mx::kBM - 1) / mx::kBM, tiles_n = (N + mx::kBN - 1) / mx::kBN;
+  // Grouped: an upper bound of row tiles, each group adding at most one
+  // partial tile, so the host never reads the device-side offsets.
+  const int64_t tiles_m = (M + mx::kBM - 1) / mx::kBM + G, tiles_n = (N + mx::kBN - 1) / mx::kBN;
   int64_t blocks;
   if (!mul_ok(tiles_m, tiles_n, &blocks) || blocks > (int64_t)INT32_MAX / mx::kGemmThreads) return MXFP8_ERR_OVERFLOW;
   mx::GemmArgs g{};
@@ -370,10 +392,33 @@ mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_s
   g.ldc = ldc;
   g.tiles_m = (int32_t)tiles_m;
   g.tiles_n = (int32_t)tiles_n;
+  g.offs = offs;
+  g.G = (int32_t)G;
+  g.stride_b = stride_b;
+  g.stride_sb = stride_sb;
   void *kargs[] = {&g};
-  hipError_t err = hipLaunchKernel((const void *)&mx::k_mx_gemm, dim3((unsigned)blocks), dim3(mx::kGemmThreads),
-                                   kargs, 0, (hipStream_t)stream);
+  const void *k = G > 0 ? (const void *)&mx::k_mx_gemm<true> : (const void *)&mx::k_mx_gemm<false>;
+  hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(mx::kGemmThreads), kargs, 0, (hipStream_t)stream);
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b, int64_t ldb,
+                        const void *sb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc,
+                        void *stream) {
+  return gemm_launch(a, lda, sa, ld_sa, b, ldb, 0, sb, ld_sb, 0, nullptr, 0, M, N, K, c, ldc, stream);
+}
+
+mxfp8_status mxfp8_grouped_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b,
+                                int64_t ldb, int64_t stride_b, const void *sb, int64_t ld_sb, int64_t stride_sb,
+                                const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K, float *c,
+                                int64_t ldc, void *stream) {
+  if (G <= 0) return G == 0 ? MXFP8_OK : MXFP8_ERR_SHAPE;
+  return gemm_launch(a, lda, sa, ld_sa, b, ldb, stride_b, sb, ld_sb, stride_sb, offsets, G, M, N, K, c, ldc,
+                     stream);
 }
 
 const char *mxfp8_status_str(mxfp8_status status) {

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_gated_fwd", "mxfp8_gated_bwd",
                      "mxfp8_quant_2d", "mxfp8_quant_3d_colwise", "mxfp8_swiglu_fwd_bf16", "mxfp8_swiglu_bwd_bf16",
-                     "mxfp8_gemm", "mxfp8_status_str"}
+                     "mxfp8_gemm", "mxfp8_grouped_gemm", "mxfp8_status_str"}
     for n in names:
         assert getattr(lib, n) is not None
 
@@ -271,3 +271,26 @@ def test_gemm_errors():
     assert gemm(c=A + 2) == ALIGN
     assert gemm(sa=A + 1, lda=120) == STRIDE        # scales need no alignment
     assert gemm(M=1 << 62, K=1 << 20, lda=1 << 20, ldb=1 << 20, ld_sa=1 << 15, ld_sb=1 << 15) == OVERFLOW
+
+
+def ggemm(**kw):
+    a = dict(a=A, lda=128, sa=A, ld_sa=4, b=A, ldb=128, stride_b=48 * 128, sb=A, ld_sb=4, stride_sb=48 * 4, offs=A,
+             G=3, M=64, N=48, K=128, c=A, ldc=48)
+    a.update(kw)
+    return mx.lib().mxfp8_grouped_gemm(a["a"], a["lda"], a["sa"], a["ld_sa"], a["b"], a["ldb"], a["stride_b"], a["sb"],
+                                       a["ld_sb"], a["stride_sb"], a["offs"], a["G"], a["M"], a["N"], a["K"], a["c"],
+                                       a["ldc"], None)
+
+
+def test_grouped_gemm_errors():
+    assert ggemm(G=0, offs=None) == OK               # no groups: nothing to do
+    assert ggemm(G=-1) == SHAPE
+    assert ggemm(G=1025) == SHAPE
+    assert ggemm(K=40) == SHAPE
+    assert ggemm(offs=None) == NULL
+    assert ggemm(stride_b=47 * 128) == STRIDE        # experts would overlap
+    assert ggemm(stride_b=48 * 128 + 8) == STRIDE    # not a multiple of 16
+    assert ggemm(stride_sb=47 * 4) == STRIDE
+    assert ggemm(offs=A + 2) == ALIGN
+    assert ggemm(lda=120) == STRIDE
+    assert ggemm(M=0, a=None) == OK

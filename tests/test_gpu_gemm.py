@@ -203,3 +203,78 @@ def test_gemm_single_products_exact_and_truncation_threshold():
     kept = c2[small] - 1.0
     assert np.all(kept[want[small] >= 2.0 ** -13] == np.trunc(want[small][want[small] >= 2.0 ** -13] * 2 ** 13) / 2 ** 13)
     assert np.all(kept[want[small] < 2.0 ** -13] == 0)
+
+
+# ------------------------------------------------------------ grouped form
+def _check_grouped(oracle_mod, name, a, sa, b, sb, offs, got, sentinel):
+    want, mag = oracle_mod.mx_grouped_gemm(a, sa, b, sb, offs)
+    got = np.asarray(got, np.float64)
+    covered = ~np.isnan(mag[:, 0]) if mag.shape[1] else np.zeros(a.shape[0], bool)
+    assert np.all(got[~covered] == sentinel), f"{name}: rows outside every group were written"
+    start = 0
+    for g in range(b.shape[0]):
+        end = int(min(max(int(offs[g]), start), a.shape[0]))
+        if end > start:
+            bound = 64 * 2.0 ** -13 * _step_max_sum(a[start:end], sa[start:end], b[g], sb[g]) \
+                + (a.shape[1] / 64 + 1) * 2.0 ** -24 * mag[start:end]
+            err = np.abs(got[start:end] - want[start:end])
+            assert np.all(err <= bound), f"{name}: group {g} beyond the bound"
+        start = end
+
+
+@pytest.mark.parametrize("offs", [[0, 300, 345, 602], [25, 10, 1000, 1000], [640, 640, 640, 640]])
+def test_grouped_gemm_random(oracle_mod, offs):
+    dev = _dev()
+    print(f"case: grouped gemm offsets {offs}", flush=True)
+    rng = np.random.default_rng(sum(offs))
+    M, N, K, G = 640, 200, 160, 4
+    a, sa = _rand_operands(rng, M, K)
+    bs = [_rand_operands(rng, N, K) for _ in range(G)]
+    b, sb = np.stack([x[0] for x in bs]), np.stack([x[1] for x in bs])
+    offs = np.array(offs, np.int32)
+    out = torch.full((M, N), -7.0, dtype=torch.float32, device=dev)
+    mx.mxfp8_grouped_gemm(_to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev),
+                          torch.from_numpy(offs).to(dev), out=out)
+    _check_grouped(oracle_mod, f"grouped{offs.tolist()}", a, sa, b, sb, offs, out.cpu().numpy(), -7.0)
+
+
+def test_grouped_gemm_one_group_is_the_plain_gemm():
+    dev = _dev()
+    rng = np.random.default_rng(11)
+    a, sa = _rand_operands(rng, 300, 256)
+    b, sb = _rand_operands(rng, 170, 256)
+    ta, tsa, tb, tsb = (_to_dev(x, dev) for x in (a, sa, b, sb))
+    plain = mx.mxfp8_gemm(ta, tsa, tb, tsb)
+    grouped = mx.mxfp8_grouped_gemm(ta, tsa, tb[None], tsb[None], torch.tensor([300], dtype=torch.int32, device=dev))
+    assert torch.equal(plain, grouped)
+
+
+def test_grouped_gemm_16640x8192x5120_g4_sampled(oracle_mod):
+    """The pages' grouped shape (16640 tokens, 4 experts of 8192 x 5120),
+    operands from the casts, uneven groups; sampled rows of every group."""
+    dev = _dev()
+    M, N, K, G = 16640, 8192, 5120, 4
+    print(f"case: grouped gemm {M}x{N}x{K} G={G}, sampled", flush=True)
+    x = synth.normal_bf16((M, K), 1.0, seed=80, device=dev)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(x, rowwise=True)
+    del x
+    w = synth.normal_bf16((G * N, K), 0.02, seed=81, device=dev)
+    qb, _, sb, _ = mx.mxfp8_quant_2d(w, rowwise=True)
+    del w
+    qb, sb = qb.view(G, N, K), sb.view(G, N, K // 32)
+    offs = np.array([3000, 7100, 12000, 16640], np.int32)
+    c = mx.mxfp8_grouped_gemm(qa, sa, qb, sb, torch.from_numpy(offs).to(dev))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 14)]))
+    cidx = torch.from_numpy(cols).to(dev)
+    start = 0
+    for g in range(G):
+        end = int(offs[g])
+        rows = np.unique(np.concatenate([[start, end - 1], rng.integers(start, end, 6)]))
+        ridx = torch.from_numpy(rows).to(dev)
+        _check(oracle_mod, f"g{g}", qa[ridx].cpu().numpy(), sa[ridx].cpu().numpy(), qb[g][cidx].cpu().numpy(),
+               sb[g][cidx].cpu().numpy(), c[ridx][:, cidx].cpu().numpy())
+        start = end
+    del qa, qb, sa, sb, c
+    torch.cuda.empty_cache()
