@@ -1,10 +1,13 @@
 """Short text summaries of rocprofv3 output for the bench workload.
 
-Two subcommands, each writing one summary file:
+Three subcommands, each writing one summary file:
 
   stats    <kernel_stats.csv>            from `rocprofv3 --kernel-trace --stats`
   traffic  <fetch_dir> <write_dir>       from two `rocprofv3 --pmc` runs, one
                                          with FETCH_SIZE, one with WRITE_SIZE
+  counters <dir> [<dir> ...]             any `rocprofv3 --pmc` runs: the mean
+                                         per dispatch of every counter for the
+                                         kernels matching --kernel
 
 Counter values are KiB per dispatch as the L2 reports them.  They are
 calibrated on the bench's device copy of the w13 tensor (a copy kernel of
@@ -169,6 +172,44 @@ def stats(csv_path, workload, experts, command, out, top=24):
         f.write("\n".join(lines) + "\n")
 
 
+def counters(dirs, pattern, command, out, simds=1024, xcds=8):
+    """Mean per dispatch of each counter over dispatches whose kernel name
+    contains `pattern`, plus two derived figures when their counters are
+    present: matrix-core utilization (MFMA busy cycles over active cycles
+    times SIMDs; GRBM_GUI_ACTIVE is summed over the XCDs) and the L2 hit
+    rate."""
+    vals = collections.defaultdict(list)
+    names = set()
+    for d in dirs:
+        for r in _counter_rows(d):
+            if pattern in r["Kernel_Name"]:
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                names.add(re.sub(r"^void |\(.*$", "", r["Kernel_Name"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel matching {pattern!r}")
+    mean = {k: sum(v) / len(v) for k, v in vals.items()}
+    lines = [
+        f"# rocprofv3 counter summary: kernels matching {pattern!r} ({', '.join(sorted(names))})",
+        *[f"# command: {c}" for c in command],
+        f"# kernel source hash (bench.py kernel_source_hash): {_build.kernel_source_hash()}",
+        "# columns: counter, mean per dispatch, dispatches",
+        "",
+    ]
+    for k in sorted(mean):
+        lines.append(f"{k:32s} {mean[k]:16.6g} {len(vals[k]):4d}")
+    derived = []
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and "GRBM_GUI_ACTIVE" in mean:
+        util = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (mean["GRBM_GUI_ACTIVE"] / xcds * simds)
+        derived.append(f"matrix-core utilization: {100 * util:.1f}% (MFMA busy cycles / (active cycles per XCD x {simds} SIMDs))")
+    if "TCC_HIT_sum" in mean and "TCC_MISS_sum" in mean:
+        hit = mean["TCC_HIT_sum"] / (mean["TCC_HIT_sum"] + mean["TCC_MISS_sum"])
+        derived.append(f"L2 hit rate: {100 * hit:.1f}%")
+    if derived:
+        lines += ["", *[f"# {x}" for x in derived]]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main(argv=None):
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--workload", default="swiglu_131072x8192_w13")
@@ -181,11 +222,16 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("fetch_dir")
     t.add_argument("write_dir")
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--kernel", required=True, help="substring of the kernel name")
     a = p.parse_args(argv)
     if a.kind == "stats":
         stats(a.csv, a.workload, a.experts, a.command, a.out)
-    else:
+    elif a.kind == "traffic":
         traffic(a.fetch_dir, a.write_dir, a.workload, a.experts, a.command, a.out)
+    else:
+        counters(a.dirs, a.kernel, a.command, a.out)
 
 
 if __name__ == "__main__":

@@ -62,3 +62,32 @@ def test_traffic_needs_the_copy(tmp_path):
     _write(str(tmp_path / "w"), "WRITE_SIZE", [("void mx::k_tiled<mx::OpBwd, true>(mx::Args)", 1.0)])
     with pytest.raises(SystemExit):
         ps.traffic(str(tmp_path / "f"), str(tmp_path / "w"), "swiglu_131072x8192_w13", 64, [], str(tmp_path / "o"))
+
+
+def test_counters_mean_and_derived_figures(tmp_path):
+    """Per-dispatch means for the matching kernel only, and the derived
+    matrix-core utilization and L2 hit rate (invented values: 8 XCDs of 1000
+    active cycles each, 1024 SIMDs busy 250 cycles each -> 25 %; 90 hits, 10
+    misses -> 90 %)."""
+    k = "void mx::k_mx_gemm<false>(mx::GemmArgs)"
+    other = "void mx::k_tiled<mx::OpBwd, true>(mx::Args)"
+    rows = []
+    for name, counter, vals in ((k, "SQ_VALU_MFMA_BUSY_CYCLES", (256000.0, 256000.0)), (k, "GRBM_GUI_ACTIVE", (8000.0, 8000.0)),
+                                (k, "TCC_HIT_sum", (80.0, 100.0)), (k, "TCC_MISS_sum", (10.0, 10.0)),
+                                (other, "TCC_HIT_sum", (1.0, 1.0))):
+        rows += [(name, counter, v) for v in vals]
+    d = tmp_path / "c"
+    os.makedirs(d)
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=FIELDS)
+        w.writeheader()
+        for i, (name, counter, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Counter_Name": counter, "Counter_Value": v})
+    out = tmp_path / "o.txt"
+    ps.counters([str(d)], "k_mx_gemm<false>", ["cmd"], str(out))
+    text = out.read_text()
+    assert "matrix-core utilization: 25.0%" in text
+    assert "L2 hit rate: 90.0%" in text
+    assert "TCC_HIT_sum                                    90    2" in text
+    with pytest.raises(SystemExit):
+        ps.counters([str(d)], "no_such_kernel", [], str(out))
