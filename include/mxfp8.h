@@ -203,7 +203,10 @@ mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *ga
  * sum into an fp32 accumulator.  So C is within sum_steps 64 * 2^-13 *
  * (largest |product| of the step) + (K/64) * 2^-24 * sum |products| of the
  * exact value.  K must be a multiple of 32 (whole blocks); M, N any.  a and
- * b 16-byte aligned.
+ * b 16-byte aligned.  Scales may sit at any byte offset; scale rows that
+ * start 16-byte aligned (sa, sb, ld_sa, ld_sb, and stride_sb in the grouped
+ * form, all multiples of 16, as the casts' outputs are when K is a multiple
+ * of 512) are fetched 16 bytes at a time, others byte by byte (slower).
  * A NaN code or a scale byte of 255 makes the sums it enters NaN.
  */
 mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa,

@@ -36,6 +36,9 @@ struct GemmArgs {
   const int32_t *offs;
   int32_t G;
   int64_t stride_b, stride_sb;
+  // scale rows start 16-byte aligned (sa, sb, ld_sa, ld_sb, stride_sb all
+  // multiples of 16): the scale table is then fetched 16 bytes at a time
+  int32_t scale_vec;
 };
 
 constexpr int kMaxGroups = 1024;
@@ -48,6 +51,8 @@ constexpr int kBK = 64;               // K per LDS stage: one MFMA step
 constexpr int kGroup = 4;             // tile rows per group in the tile order
 constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 64 of C
 constexpr int kStageA = kBM * kBK, kStageB = kBN * kBK;  // one stage of each operand in LDS (bytes)
+constexpr int kSG = 16;                                  // scale blocks per LDS scale group (kSG / 2 stages)
+static_assert(kSG / 2 >= 2, "a scale group is written to LDS in its second stage");
 
 __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
   return *gptr(reinterpret_cast<const u32x4_t *>(p));
@@ -62,6 +67,9 @@ __device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((k
 template <bool GROUPED>
 __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smemA[2][kStageA], smemB[2][kStageB];  // [buffer]
+  // scale table of one group of kSG blocks: row q < kBM is A's tile row q,
+  // row kBM + q is B's tile row q  [buffer][row][block]
+  __shared__ __attribute__((aligned(16))) uint8_t smemS[2][kBM + kBN][kSG];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
 
@@ -110,14 +118,43 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
   const u32 ld_row = (u32)t >> 2, ld_kc = (u32)t & 3u;
   const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
 
-  // ---- scales: lane r + 32 h carries the scale of block h of the step for
-  // its row of each 32-row tile
+  // ---- scales: moved to LDS kSG blocks (kSG / 2 stages) at a time, thread
+  // t taking A's tile row t and, for t < kBN, B's tile row t.  Blocks past
+  // K / 32 read as 127 (2^0) against zero data.  One byte load per lane per
+  // operand tile and stage, from 32 rows at once, is far slower than this.
   const uint8_t *sa_tile = g.sa + m_base * g.ld_sa, *sb_tile = sb_mat + n_base * g.ld_sb;  // uniform
   const int64_t nblk = g.K / 32;
   const int nstage = (int)((g.K + kBK - 1) / kBK);
+  const int ngroup = (int)((nblk + kSG - 1) / kSG);
+  const u32 sa_row = min((u32)t, a_rows - 1), sb_row = min((u32)t, b_rows - 1);
 
   u32x4_t sta[4], stb[2];  // the next stage, global -> registers -> LDS
-  int nsa[4], nsb[2];      // its scale bytes per 32-row tile
+  u32x4_t ssa, ssb;        // the next scale group, global -> registers -> LDS
+  auto load_scales = [&](int grp) {
+    const int64_t b0 = (int64_t)grp * kSG;
+    if (g.scale_vec && b0 + kSG <= nblk) {  // uniform
+      ssa = gload16(byte_off(sa_tile + b0, sa_row * (u32)g.ld_sa));
+      if (t < kBN) ssb = gload16(byte_off(sb_tile + b0, sb_row * (u32)g.ld_sb));
+    } else {
+      // byte by byte, from clamped (in-bounds) positions; blocks past K / 32 read as 127
+      u32 wa[4] = {0, 0, 0, 0}, wb[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int j = 0; j < kSG; j++) {
+        const bool ok = b0 + j < nblk;
+        const int64_t bj = min<int64_t>(b0 + j, nblk - 1);
+        const u32 va = *gptr(byte_off(sa_tile + bj, sa_row * (u32)g.ld_sa));
+        const u32 vb = *gptr(byte_off(sb_tile + bj, sb_row * (u32)g.ld_sb));
+        wa[j / 4] |= (ok ? va : 127u) << (8 * (j % 4));
+        wb[j / 4] |= (ok ? vb : 127u) << (8 * (j % 4));
+      }
+      ssa = u32x4_t{wa[0], wa[1], wa[2], wa[3]};
+      ssb = u32x4_t{wb[0], wb[1], wb[2], wb[3]};
+    }
+  };
+  auto store_scales = [&](int buf) {
+    *reinterpret_cast<u32x4_t *>(&smemS[buf][t][0]) = ssa;
+    if (t < kBN) *reinterpret_cast<u32x4_t *>(&smemS[buf][kBM + t][0]) = ssb;
+  };
   auto load_stage = [&](int st) {
     const int64_t k0 = (int64_t)st * kBK;
     const bool kc_ok = k0 + 16 * (int64_t)ld_kc < g.K;  // whole 16-byte chunks (K % 32 == 0)
@@ -130,18 +167,6 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
     for (int j = 0; j < 2; j++) {
       const u32 rb = min(ld_row + 64u * j, b_rows - 1);
       stb[j] = kc_ok ? gload16(byte_off(b_tile + k0, rb * (u32)g.ldb + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
-    }
-    const int64_t kb = k0 / 32;  // + h below
-    const bool ok = kb + h < nblk;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const u32 ra = min((u32)(wm * 128 + 32 * i + r), a_rows - 1);
-      nsa[i] = ok ? (int)*gptr(byte_off(sa_tile + kb, ra * (u32)g.ld_sa + (u32)h)) : 127;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const u32 rb = min((u32)(wn * 64 + 32 * j + r), b_rows - 1);
-      nsb[j] = ok ? (int)*gptr(byte_off(sb_tile + kb, rb * (u32)g.ld_sb + (u32)h)) : 127;
     }
   };
   auto store_stage = [&](int buf) {
@@ -157,19 +182,31 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 2; j++) acc[i][j] = v16f_t{};
 
-  int csa[4], csb[2];
   load_stage(0);
+  if (ngroup > 0) load_scales(0);  // K = 0: no scale is read
   store_stage(0);
-#pragma unroll
-  for (int i = 0; i < 4; i++) csa[i] = nsa[i];
-#pragma unroll
-  for (int j = 0; j < 2; j++) csb[j] = nsb[j];
+  if (ngroup > 0) store_scales(0);
   __syncthreads();
 
   for (int st = 0; st < nstage; st++) {
     const int buf = st & 1;
     const bool more = st + 1 < nstage;  // uniform
+    const int grp = st / (kSG / 2), in_grp = st % (kSG / 2);
+    const bool more_scales = grp + 1 < ngroup;  // uniform
+    // the next scale group: fetched in the group's first stage, written to
+    // LDS at the start of its second (the fetch completed with the first
+    // stage's data), into the buffer whose last reads ended with the
+    // previous group; first read after a later barrier
+    if (more_scales && in_grp == 1) store_scales((grp + 1) & 1);
     if (more) load_stage(st + 1);
+    if (more_scales && in_grp == 0) load_scales(grp + 1);
+    // this stage's scales: lane r + 32 h takes block 2 in_grp + h of its row
+    // in each 32-row tile
+    int csa[4], csb[2];
+#pragma unroll
+    for (int i = 0; i < 4; i++) csa[i] = smemS[grp & 1][wm * 128 + 32 * i + r][2 * in_grp + h];
+#pragma unroll
+    for (int j = 0; j < 2; j++) csb[j] = smemS[grp & 1][kBM + wn * 64 + 32 * j + r][2 * in_grp + h];
     v8i_t bv[2];
 #pragma unroll
     for (int j = 0; j < 2; j++) {
@@ -188,13 +225,14 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
       for (int j = 0; j < 2; j++)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], 0, 0, 0, csa[i], 0, csb[j]);
     }
-    if (more) {
-      store_stage(buf ^ 1);
-#pragma unroll
-      for (int i = 0; i < 4; i++) csa[i] = nsa[i];
-#pragma unroll
-      for (int j = 0; j < 2; j++) csb[j] = nsb[j];
-    }
+    // The next stage's LDS writes, and with them the waits for its global
+    // loads, stay after this stage's MFMAs: hoisted above them, the loads'
+    // latency is exposed in every stage.  They are not behind `more`, so
+    // that the MFMAs cannot sink into a later block past the scheduling
+    // barrier; on the last stage they rewrite the idle buffer, whose last
+    // reads ended at the previous barrier, with data no one reads.
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage(buf ^ 1);
     __syncthreads();
   }
 

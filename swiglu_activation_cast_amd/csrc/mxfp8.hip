@@ -396,6 +396,7 @@ mxfp8_status gemm_launch(const void *a, int64_t lda, const void *sa, int64_t ld_
   g.G = (int32_t)G;
   g.stride_b = stride_b;
   g.stride_sb = stride_sb;
+  g.scale_vec = aligned16(sa) && aligned16(sb) && ld_sa % 16 == 0 && ld_sb % 16 == 0 && stride_sb % 16 == 0;
   void *kargs[] = {&g};
   const void *k = G > 0 ? (const void *)&mx::k_mx_gemm<true> : (const void *)&mx::k_mx_gemm<false>;
   hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(mx::kGemmThreads), kargs, 0, (hipStream_t)stream);

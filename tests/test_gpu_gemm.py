@@ -74,7 +74,7 @@ def _to_dev(x, dev):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (37, 45, 96), (128, 128, 64), (200, 130, 256), (256, 384, 1024),
-                                   (64, 300, 4096)])
+                                   (64, 300, 4096), (300, 140, 1120)])
 def test_gemm_random_codes(oracle_mod, M, N, K):
     dev = _dev()
     print(f"case: gemm random codes M={M} N={N} K={K}", flush=True)
@@ -117,12 +117,13 @@ def test_gemm_nan_blocks(oracle_mod):
     _check(oracle_mod, "nan", a, sa, b, sb, c.cpu().numpy())
 
 
-def test_gemm_strided_and_guarded(oracle_mod):
-    """Operands carved out of wider buffers; C written into a padded buffer
-    whose padding stays untouched."""
+@pytest.mark.parametrize("K", [160, 1056])
+def test_gemm_strided_and_guarded(oracle_mod, K):
+    """Operands carved out of wider buffers (scale rows at odd byte
+    offsets); C written into a padded buffer whose padding stays untouched."""
     dev = _dev()
-    rng = np.random.default_rng(8)
-    M, N, K = 70, 90, 160
+    rng = np.random.default_rng(8 + K)
+    M, N = 70, 90
     abig, sabig = _rand_operands(rng, M, K + 64)
     bbig, sbbig = _rand_operands(rng, N, K + 96)
     a, sa = abig[:, 32:32 + K], sabig[:, 1:1 + K // 32]
@@ -222,12 +223,13 @@ def _check_grouped(oracle_mod, name, a, sa, b, sb, offs, got, sentinel):
         start = end
 
 
+@pytest.mark.parametrize("K", [160, 1120])
 @pytest.mark.parametrize("offs", [[0, 300, 345, 602], [25, 10, 1000, 1000], [640, 640, 640, 640]])
-def test_grouped_gemm_random(oracle_mod, offs):
+def test_grouped_gemm_random(oracle_mod, offs, K):
     dev = _dev()
-    print(f"case: grouped gemm offsets {offs}", flush=True)
-    rng = np.random.default_rng(sum(offs))
-    M, N, K, G = 640, 200, 160, 4
+    print(f"case: grouped gemm offsets {offs} K={K}", flush=True)
+    rng = np.random.default_rng(sum(offs) + K)
+    M, N, G = 640, 200, 4
     a, sa = _rand_operands(rng, M, K)
     bs = [_rand_operands(rng, N, K) for _ in range(G)]
     b, sb = np.stack([x[0] for x in bs]), np.stack([x[1] for x in bs])
