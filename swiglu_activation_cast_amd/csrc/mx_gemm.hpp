@@ -19,6 +19,13 @@
 // lane m + 32 b (op_sel picks the register byte).  The 32x32 fp32 result
 // sits in 16 registers: lane l, register v holds row 8 (v / 4) + 4 (l / 32)
 // + v % 4, column l % 32.
+//
+// Structure: a 256 x 256 C tile per 256-thread workgroup, one workgroup per
+// CU (148 KB of LDS); each wavefront owns 128 x 128 of C, its 256
+// accumulators in AGPRs.  K is staged 128 at a time (two MFMA steps) in a
+// double-buffered LDS ring filled by direct global -> LDS loads; each stage
+// reads all its operands from LDS, then issues the next stage's loads, then
+// its 32 MFMAs, so the loads run under the matrix work.
 #pragma once
 #include "mx_kernels.hpp"
 
@@ -43,29 +50,33 @@ struct GemmArgs {
 
 constexpr int kMaxGroups = 1024;
 
+// 16 zero bytes in device memory: the source of operand chunks at or past K
+__device__ __attribute__((aligned(16))) const uint8_t kZeroChunk[16] = {};
+
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 256, kBN = 128;  // C tile per workgroup
-constexpr int kBK = 64;               // K per LDS stage: one MFMA step
+constexpr int kBM = 256, kBN = 256;  // C tile per workgroup
+constexpr int kBK = 128;              // K per LDS stage: two MFMA steps, whole 128-byte lines
 constexpr int kGroup = 4;             // tile rows per group in the tile order
-constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 64 of C
+constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 128 of C
 constexpr int kStageA = kBM * kBK, kStageB = kBN * kBK;  // one stage of each operand in LDS (bytes)
-constexpr int kSG = 16;                                  // scale blocks per LDS scale group (kSG / 2 stages)
-static_assert(kSG / 2 >= 2, "a scale group is written to LDS in its second stage");
+constexpr int kSG = 16;                                  // scale blocks per LDS scale group
+constexpr int kStagesPerGroup = kSG / (kBK / 32);
+static_assert(kStagesPerGroup >= 2, "a scale group is written to LDS in its second stage");
 
 __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
   return *gptr(reinterpret_cast<const u32x4_t *>(p));
 }
 
-// LDS position of 16-byte chunk kc (0..3) of tile row `row`: rows of 64
-// bytes, chunks XOR-permuted by (row / 4) % 4, so that the 16 lanes of one
+// LDS position of 16-byte chunk kc (0..7) of tile row `row`: rows of 128
+// bytes, chunks XOR-permuted by (row / 2) % 8, so that the 16 lanes of one
 // quarter-wave reading the same chunk of 16 consecutive rows hit 16
-// different 4-bank groups, and 4 lanes writing one row cover it once.
-__device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 2) & 3u)) << 4); }
+// different 4-bank groups.
+__device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 1) & 7u)) << 4); }
 
 template <bool GROUPED>
-__global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smemA[2][kStageA], smemB[2][kStageB];  // [buffer]
   // scale table of one group of kSG blocks: row q < kBM is A's tile row q,
   // row kBM + q is B's tile row q  [buffer][row][block]
@@ -111,30 +122,26 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
     sb_mat = g.sb + (int64_t)e_hit * g.stride_sb;
   }
 
-  // ---- global -> LDS assignment: thread t moves chunk t % 4 of tile rows
-  // t / 4 + 64 j of A (j = 0..3) and of B (j = 0..1).  Rows past M (N) are read as the
-  // last row: in bounds, never stored.
+  // Rows past M (N) are read as the last row: in bounds, never stored.
   const uint8_t *a_tile = g.a + m_base * g.lda, *b_tile = b_mat + n_base * g.ldb;  // uniform
-  const u32 ld_row = (u32)t >> 2, ld_kc = (u32)t & 3u;
   const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
 
-  // ---- scales: moved to LDS kSG blocks (kSG / 2 stages) at a time, thread
-  // t taking A's tile row t and, for t < kBN, B's tile row t.  Blocks past
-  // K / 32 read as 127 (2^0) against zero data.  One byte load per lane per
-  // operand tile and stage, from 32 rows at once, is far slower than this.
+  // ---- scales: moved to LDS kSG blocks (kStagesPerGroup stages) at a
+  // time, thread t taking A's and B's tile row t.  Blocks past K / 32 read
+  // as 127 (2^0) against zero data.  One byte load per lane per operand
+  // tile and stage, from 32 rows at once, is far slower than this.
   const uint8_t *sa_tile = g.sa + m_base * g.ld_sa, *sb_tile = sb_mat + n_base * g.ld_sb;  // uniform
   const int64_t nblk = g.K / 32;
   const int nstage = (int)((g.K + kBK - 1) / kBK);
   const int ngroup = (int)((nblk + kSG - 1) / kSG);
   const u32 sa_row = min((u32)t, a_rows - 1), sb_row = min((u32)t, b_rows - 1);
 
-  u32x4_t sta[4], stb[2];  // the next stage, global -> registers -> LDS
-  u32x4_t ssa, ssb;        // the next scale group, global -> registers -> LDS
+  u32x4_t ssa, ssb;  // the next scale group, global -> registers -> LDS
   auto load_scales = [&](int grp) {
     const int64_t b0 = (int64_t)grp * kSG;
     if (g.scale_vec && b0 + kSG <= nblk) {  // uniform
       ssa = gload16(byte_off(sa_tile + b0, sa_row * (u32)g.ld_sa));
-      if (t < kBN) ssb = gload16(byte_off(sb_tile + b0, sb_row * (u32)g.ld_sb));
+      ssb = gload16(byte_off(sb_tile + b0, sb_row * (u32)g.ld_sb));
     } else {
       // byte by byte, from clamped (in-bounds) positions; blocks past K / 32 read as 127
       u32 wa[4] = {0, 0, 0, 0}, wb[4] = {0, 0, 0, 0};
@@ -153,94 +160,109 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_mx_gemm(const GemmArgs g) {
   };
   auto store_scales = [&](int buf) {
     *reinterpret_cast<u32x4_t *>(&smemS[buf][t][0]) = ssa;
-    if (t < kBN) *reinterpret_cast<u32x4_t *>(&smemS[buf][kBM + t][0]) = ssb;
+    *reinterpret_cast<u32x4_t *>(&smemS[buf][kBM + t][0]) = ssb;
   };
-  auto load_stage = [&](int st) {
-    const int64_t k0 = (int64_t)st * kBK;
-    const bool kc_ok = k0 + 16 * (int64_t)ld_kc < g.K;  // whole 16-byte chunks (K % 32 == 0)
+  // ---- operands: global -> LDS directly (global_load_lds_dwordx4: lane
+  // l's 16 bytes land at the instruction's LDS base + 16 l).  Wave w fills
+  // 1 KB slabs p = 8 w + q (q = 0..7) of each operand's stage buffer, i.e.
+  // tile rows 8 p .. 8 p + 7; lane l writes slab bytes 16 l .. 16 l + 15,
+  // which hold row 8 p + l / 8, stored chunk l % 8, i.e. logical chunk
+  // (l % 8) ^ the row's XOR key.  Chunks at or past K, and so every chunk
+  // of a stage past the last, are read from kZeroChunk.
+  auto dma_stage = [&](int st_, int buf_) {
+    const int64_t k0 = (int64_t)st_ * kBK;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const u32 ra = min(ld_row + 64u * j, a_rows - 1);
-      sta[j] = kc_ok ? gload16(byte_off(a_tile + k0, ra * (u32)g.lda + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
+    for (int q = 0; q < 8; q++) {
+      const u32 p = (u32)w * 8u + (u32)q;
+      const u32 row = 8u * p + ((u32)lane >> 3), kc = ((u32)lane & 7u) ^ ((row >> 1) & 7u);
+      const bool in_k = k0 + 16 * (int64_t)kc < g.K;
+      const u32 ra = min(row, a_rows - 1), rb = min(row, b_rows - 1);
+      const uint8_t *pa = in_k ? byte_off(a_tile + k0, ra * (u32)g.lda + kc * 16u) : kZeroChunk;
+      const uint8_t *pb = in_k ? byte_off(b_tile + k0, rb * (u32)g.ldb + kc * 16u) : kZeroChunk;
+      __builtin_amdgcn_global_load_lds((const MX_GLOBAL void *)gptr(pa),
+                                       (__attribute__((address_space(3))) void *)&smemA[buf_][p * 1024u], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const MX_GLOBAL void *)gptr(pb),
+                                       (__attribute__((address_space(3))) void *)&smemB[buf_][p * 1024u], 16, 0, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const u32 rb = min(ld_row + 64u * j, b_rows - 1);
-      stb[j] = kc_ok ? gload16(byte_off(b_tile + k0, rb * (u32)g.ldb + ld_kc * 16u)) : u32x4_t{0, 0, 0, 0};
-    }
   };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; j++) *reinterpret_cast<u32x4_t *>(&smemA[buf][lds_off(ld_row + 64u * j, ld_kc)]) = sta[j];
-#pragma unroll
-    for (int j = 0; j < 2; j++) *reinterpret_cast<u32x4_t *>(&smemB[buf][lds_off(ld_row + 64u * j, ld_kc)]) = stb[j];
-  };
+  constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters not waited
 
-  v16f_t acc[4][2];
+  v16f_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = v16f_t{};
+    for (int j = 0; j < 4; j++) acc[i][j] = v16f_t{};
 
-  load_stage(0);
+  if (nstage > 0) dma_stage(0, 0);
   if (ngroup > 0) load_scales(0);  // K = 0: no scale is read
-  store_stage(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   if (ngroup > 0) store_scales(0);
   __syncthreads();
 
   for (int st = 0; st < nstage; st++) {
     const int buf = st & 1;
-    const bool more = st + 1 < nstage;  // uniform
-    const int grp = st / (kSG / 2), in_grp = st % (kSG / 2);
+    const int grp = st / kStagesPerGroup, in_grp = st % kStagesPerGroup;
     const bool more_scales = grp + 1 < ngroup;  // uniform
     // the next scale group: fetched in the group's first stage, written to
     // LDS at the start of its second (the fetch completed with the first
     // stage's data), into the buffer whose last reads ended with the
     // previous group; first read after a later barrier
     if (more_scales && in_grp == 1) store_scales((grp + 1) & 1);
-    if (more) load_stage(st + 1);
     if (more_scales && in_grp == 0) load_scales(grp + 1);
-    // this stage's scales: lane r + 32 h takes block 2 in_grp + h of its row
-    // in each 32-row tile
-    int csa[4], csb[2];
+    // this stage's operands and scales for both MFMA steps, all read before
+    // the first MFMA in the order the MFMAs consume them; in step s lane
+    // r + 32 h takes block 4 in_grp + 2 s + h of its row in each 32-row tile
+    int csa[2][4], csb[2][4];
+    v8i_t av[2][4], bv[2][4];
+    auto read_op = [&](const uint8_t *base, u32 row, u32 s) {
+      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&base[lds_off(row, 4u * s + h)]);
+      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&base[lds_off(row, 4u * s + 2u + h)]);
+      return v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    };
 #pragma unroll
-    for (int i = 0; i < 4; i++) csa[i] = smemS[grp & 1][wm * 128 + 32 * i + r][2 * in_grp + h];
+    for (int s = 0; s < 2; s++) {
 #pragma unroll
-    for (int j = 0; j < 2; j++) csb[j] = smemS[grp & 1][kBM + wn * 64 + 32 * j + r][2 * in_grp + h];
-    v8i_t bv[2];
+      for (int i = 0; i < 4; i++) csa[s][i] = smemS[grp & 1][wm * 128 + 32 * i + r][4 * in_grp + 2 * s + h];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const u32 row = (u32)(wn * 64 + 32 * j + r);
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smemB[buf][lds_off(row, (u32)h)]);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smemB[buf][lds_off(row, 2u + h)]);
-      bv[j] = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int j = 0; j < 4; j++) csb[s][j] = smemS[grp & 1][kBM + wn * 128 + 32 * j + r][4 * in_grp + 2 * s + h];
+      av[s][0] = read_op(smemA[buf], (u32)(wm * 128 + r), s);
+#pragma unroll
+      for (int j = 0; j < 4; j++) bv[s][j] = read_op(smemB[buf], (u32)(wn * 128 + 32 * j + r), s);
+#pragma unroll
+      for (int i = 1; i < 4; i++) av[s][i] = read_op(smemA[buf], (u32)(wm * 128 + 32 * i + r), s);
     }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const u32 row = (u32)(wm * 128 + 32 * i + r);
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&smemA[buf][lds_off(row, (u32)h)]);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&smemA[buf][lds_off(row, 2u + h)]);
-      const v8i_t av = v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-#pragma unroll
-      for (int j = 0; j < 2; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[j], acc[i][j], 0, 0, 0, csa[i], 0, csb[j]);
-    }
-    // The next stage's LDS writes, and with them the waits for its global
-    // loads, stay after this stage's MFMAs: hoisted above them, the loads'
-    // latency is exposed in every stage.  They are not behind `more`, so
-    // that the MFMAs cannot sink into a later block past the scheduling
-    // barrier; on the last stage they rewrite the idle buffer, whose last
-    // reads ended at the previous barrier, with data no one reads.
     __builtin_amdgcn_sched_barrier(0);
-    store_stage(buf ^ 1);
+    // The next stage's loads, into the other buffer (its last reads ended at
+    // the previous barrier), issued after every LDS read of this stage: the
+    // compiler waits for such loads before any later LDS read.  Not behind
+    // a branch, so that the MFMAs cannot sink past the scheduling barriers
+    // into a later block (after the last stage it loads zeros into the idle
+    // buffer).
+    dma_stage(st + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[0][i], bv[0][j], acc[i][j], 0, 0, 0, csa[0][i],
+                                                                     0, csb[0][j]);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[1][i], bv[1][j], acc[i][j], 0, 0, 0, csa[1][i],
+                                                                     0, csb[1][j]);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads have landed; the barrier makes every wave's visible
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
   }
 
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int64_t col = n_base + wn * 64 + 32 * j + r;
+    for (int j = 0; j < 4; j++) {
+      const int64_t col = n_base + wn * 128 + 32 * j + r;
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
