@@ -1,15 +1,18 @@
-"""Generates the erfc polynomial used by the exact-GELU gate (mx_ops.hpp).
+"""Generates the erfc polynomials used by the exact-GELU gate (mx_ops.hpp).
 
-For z >= 0 the kernel evaluates
+For z >= 0 the kernel evaluates, with t = 2 / (2 + z) and x = 2t - 1 in (-1, 1],
 
-    erfc(z) = t * exp(-z^2 + P(x)),   t = 2 / (2 + z),   x = 2t - 1 in (-1, 1],
+    erfc(z) = t * exp(-z^2 + P(x))    (forward: one exponential)
+    erfc(z) = t * exp(-z^2) * Q(x)    (backward: the exponential is shared
+                                       with the Gaussian in the derivative)
 
 the change of variable of Schonfelder's Chebyshev expansions of the error
 function ("Chebyshev expansions for the error and related functions", Math.
 Comp. 32, 1978), which maps the whole half-line onto one interval on which
-P(x) = ln(erfcx(z) (2 + z) / 2) is smooth.  P is fitted here by least squares
-on Chebyshev nodes in double precision (scipy's erfcx as the target),
-converted to the power basis for Horner evaluation, and rounded to float32.
+Q(x) = erfcx(z) (2 + z) / 2 (between 1/(2 sqrt(pi)) and 1) and its logarithm
+P(x) are smooth.  Each is fitted here by least squares on Chebyshev nodes in
+double precision (scipy's erfcx as the target), converted to the power basis
+for Horner evaluation, and rounded to float32.
 
 Run `python gen_erfc_fit.py` to print the constants; `tests/test_erfc_fit.py`
 checks that the header holds exactly these values and bounds the float32
@@ -19,33 +22,35 @@ from __future__ import annotations
 
 import numpy as np
 
-DEGREE = 9
+DEGREE = {"P": 9, "Q": 10}
 NODES = 40001
 
 
-def fit(degree: int = DEGREE) -> tuple[np.ndarray, float]:
-    """Power-basis coefficients (lowest first, float64) and the max fit error."""
+def fit(which: str = "P") -> tuple[np.ndarray, float]:
+    """Power-basis coefficients (lowest first, float64) of P or Q and the max
+    fit error (absolute in P, relative in Q: relative in erfc either way)."""
     from scipy.special import erfcx
 
     x = np.cos(np.linspace(0.0, np.pi, NODES))
     x = x[x > -1.0 + 1e-12]                  # x = -1 is z = infinity
     z = 2.0 * (1.0 - x) / (1.0 + x)          # inverse of x = 4 / (2 + z) - 1
-    y = np.log(erfcx(z) * (2.0 + z) / 2.0)
-    cheb = np.polynomial.chebyshev.chebfit(x, y, degree)
+    q = erfcx(z) * (2.0 + z) / 2.0
+    y = np.log(q) if which == "P" else q
+    cheb = np.polynomial.chebyshev.chebfit(x, y, DEGREE[which])
     power = np.polynomial.chebyshev.cheb2poly(cheb)
-    err = float(np.abs(np.polynomial.polynomial.polyval(x, power) - y).max())
-    return power, err
+    err = np.abs(np.polynomial.polynomial.polyval(x, power) - y)
+    return power, float((err if which == "P" else err / y).max())
 
 
-def float32_coefficients(degree: int = DEGREE) -> list[float]:
-    power, _ = fit(degree)
+def float32_coefficients(which: str = "P") -> list[float]:
+    power, _ = fit(which)
     return [float(np.float32(c)) for c in power]
 
 
-def c_literals(degree: int = DEGREE) -> list[str]:
+def c_literals(which: str = "P") -> list[str]:
     """The coefficients as C hexadecimal float literals (exact float32 values)."""
     out = []
-    for c in float32_coefficients(degree):
+    for c in float32_coefficients(which):
         mant, exp = c.hex().split("p")
         mant = mant.rstrip("0").rstrip(".")
         out.append(f"{mant}p{exp}f")
@@ -53,6 +58,7 @@ def c_literals(degree: int = DEGREE) -> list[str]:
 
 
 if __name__ == "__main__":
-    _, err = fit()
-    print(f"// degree {DEGREE}, max |fit error| {err:.2e} (absolute in P, relative in erfc)")
-    print("constexpr float kErfcP[%d] = {%s};" % (DEGREE + 1, ", ".join(c_literals())))
+    for which in ("P", "Q"):
+        _, err = fit(which)
+        print(f"// {which}: degree {DEGREE[which]}, max fit error {err:.2e} (relative in erfc)")
+        print("constexpr float kErfc%s[%d] = {%s};" % (which, DEGREE[which] + 1, ", ".join(c_literals(which))))

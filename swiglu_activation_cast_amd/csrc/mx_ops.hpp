@@ -59,6 +59,10 @@ struct ActSilu {
     return s;
   }
 
+  // the backward recomputes the activation as the forward does
+  template <bool careful>
+  __device__ __forceinline__ static float bwd_act(float g) { return act<careful>(g); }
+
   template <bool careful>
   __device__ __forceinline__ static float dgate(float da, float g) {
     const float sig = sigmoid_near(g);
@@ -89,6 +93,10 @@ struct ActGeluTanh {
     return a;
   }
 
+  // the backward recomputes the activation as the forward does
+  template <bool careful>
+  __device__ __forceinline__ static float bwd_act(float g) { return act<careful>(g); }
+
   template <bool careful>
   __device__ __forceinline__ static float dgate(float da, float g) {
     const float wv = w(g), sig = sigmoid_near(wv), d = dw(g);
@@ -109,17 +117,23 @@ struct ActGeluTanh {
 // GELU, exact form: g Phi(g), Phi(g) = erfc(-g / sqrt 2) / 2 (the normal
 // cdf); derivative Phi(g) + g phi(g), phi(g) = e^(-g^2/2) / sqrt(2 pi).
 //
-// erfc(z) for z = |g| / sqrt 2 >= 0 is t e^(-z^2 + P(x)) with t = 2 / (2 + z)
-// and x = 2t - 1: the change of variable of Schonfelder's Chebyshev
-// expansions of the error function, which maps z in [0, inf) onto x in
-// (-1, 1], where P(x) = ln(erfcx(z) (2 + z) / 2) is smooth.  P is the degree-9
-// least-squares fit printed by gen_erfc_fit.py (fit error 1.0e-7 absolute in
-// P, so relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
-// exact for a bf16 g, so e^(-z^2 + P) is a single exponential; Phi(g) is
-// erfc(z) / 2 for g < 0 and 1 - erfc(z) / 2 otherwise.  For g < -8 the
-// exponentials are formed times 2^64 (2^-64 applied last).
+// erfc(z) for z = |g| / sqrt 2 >= 0 is t e^(-z^2) Q(x) = t e^(-z^2 + P(x))
+// with t = 2 / (2 + z) and x = 2t - 1: the change of variable of
+// Schonfelder's Chebyshev expansions of the error function, which maps z in
+// [0, inf) onto x in (-1, 1], where Q(x) = erfcx(z) (2 + z) / 2 and
+// P(x) = ln Q(x) are smooth.  P (degree 9) and Q (degree 10) are the
+// least-squares fits printed by gen_erfc_fit.py (fit errors 1.0e-7 and
+// 1.2e-8, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
+// exact for a bf16 g.  The forward forms e^(-z^2 + P) with one exponential;
+// the backward forms e^(-z^2) once for both the cdf (times Q) and the
+// Gaussian of the derivative.  Phi(g) is erfc(z) / 2 for g < 0 and
+// 1 - erfc(z) / 2 otherwise.  For g < -8 the exponentials are formed times
+// 2^64 (2^-64 applied last).
 constexpr float kErfcP[10] = {-0x1.57f564p-1f, 0x1.58649p-1f, 0x1.83d5bp-5f, -0x1.7fffc4p-5f, -0x1.438b2ep-7f,
                               0x1.1d34dep-7f, 0x1.d1b74cp-10f, -0x1.0c8826p-9f, -0x1.b404a2p-13f, 0x1.5df29ep-12f};
+constexpr float kErfcQ[11] = {0x1.058672p-1f,  0x1.5fd384p-2f,   0x1.1e2dc4p-3f,  0x1.2a8b38p-6f,
+                              -0x1.604f2ep-7f, -0x1.a9203p-9f,   0x1.90dcp-10f,   0x1.c39742p-12f,
+                              -0x1.39ececp-12f, -0x1.330a0ap-15f, 0x1.61ac72p-15f};
 
 struct ActGelu {
   static constexpr float kRsqrt2 = 0.7071067811865476f;
@@ -144,6 +158,20 @@ struct ActGelu {
     return g < 0.0f ? q : 1.0f - q;
   }
 
+  // erfc(|g| / sqrt 2) / 2 from e = e^(-g^2/2) (times 2^64 if e is)
+  __device__ __forceinline__ static float half_erfc_q(float g, float e) {
+    const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
+    const float x = __builtin_fmaf(th, 4.0f, -1.0f);
+    float q = kErfcQ[10];
+#pragma unroll
+    for (int i = 9; i >= 0; i--) q = __builtin_fmaf(q, x, kErfcQ[i]);
+    return (th * q) * e;
+  }
+  __device__ __forceinline__ static float cdf_q(float g, float e) {
+    const float q = half_erfc_q(g, e);
+    return g < 0.0f ? q : 1.0f - q;
+  }
+
   // e^(-g^2/2) (g^2 is exact for a bf16 g), times 2^64 when `scaled`
   template <bool scaled>
   __device__ __forceinline__ static float gauss(float g) {
@@ -158,10 +186,23 @@ struct ActGelu {
     return a;
   }
 
+  // the activation as the backward recomputes it: from the same e^(-g^2/2)
+  // as dgate below, so that the two share one exponential
+  template <bool careful>
+  __device__ __forceinline__ static float bwd_act(float g) {
+    float a = g * cdf_q(g, gauss<false>(g));
+    if (careful && g < kFarG) a = (g * half_erfc_q(g, gauss<true>(g))) * k2m64;
+    return a;
+  }
+
   template <bool careful>
   __device__ __forceinline__ static float dgate(float da, float g) {
-    float r = da * (cdf(g) + g * (kRsqrt2Pi * gauss<false>(g)));
-    if (careful && g < kFarG) r = (da * (half_erfc<true>(g) + g * (kRsqrt2Pi * gauss<true>(g)))) * k2m64;
+    const float e = gauss<false>(g);
+    float r = da * (cdf_q(g, e) + g * (kRsqrt2Pi * e));
+    if (careful && g < kFarG) {
+      const float es = gauss<true>(g);
+      r = (da * (half_erfc_q(g, es) + g * (kRsqrt2Pi * es))) * k2m64;
+    }
     return r;
   }
 };
@@ -176,6 +217,10 @@ struct ActRelu {
   __device__ __forceinline__ static float act(float g) {
     return g <= 0.0f ? 0.0f : g;
   }
+
+  // the backward recomputes the activation as the forward does
+  template <bool careful>
+  __device__ __forceinline__ static float bwd_act(float g) { return act<careful>(g); }
 
   template <bool careful>
   __device__ __forceinline__ static float dgate(float da, float g) {
@@ -213,7 +258,7 @@ struct GatedBwd {
 
   template <bool careful>
   __device__ __forceinline__ static void elem(float dhv, float gv, float uv, float &dg, float &du) {
-    const float a = round_bf16(Act::template act<careful>(gv));
+    const float a = round_bf16(Act::template bwd_act<careful>(gv));
     du = dhv * a;
     const float da = round_bf16(dhv * uv);
     dg = Act::template dgate<careful>(da, gv);

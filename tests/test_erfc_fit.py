@@ -1,12 +1,13 @@
-"""The exact-GELU gate's erfc polynomial (host-side checks, no GPU).
+"""The exact-GELU gate's erfc polynomials (host-side checks, no GPU).
 
 - The constants in csrc/mx_ops.hpp are exactly what gen_erfc_fit.py prints.
 - The kernel's float32 evaluation, emulated step by step in numpy float32,
   stays within 1e-5 relative of the normal cdf (scipy) for GELU's value
   over every finite bf16 gate whose result is a normal float, and within a
-  small absolute error for the derivative.  (The hardware exp2 and
-  reciprocal carry about one ulp more than numpy's correctly rounded ones;
-  the bounds leave room for that.)
+  small absolute error for the derivative: the forward's form
+  t e^(-z^2 + P(x)) and the backward's t e^(-z^2) Q(x) alike.  (The hardware
+  exp2 and reciprocal carry about one ulp more than numpy's correctly
+  rounded ones; the bounds leave room for that.)
 """
 import importlib.util
 import os
@@ -28,26 +29,30 @@ def _gen():
     return mod
 
 
-def header_coefficients():
+def header_coefficients(which="P"):
     text = open(os.path.join(CSRC, "mx_ops.hpp")).read()
-    m = re.search(r"kErfcP\[(\d+)\]\s*=\s*\{([^}]*)\}", text)
-    assert m, "kErfcP not found in mx_ops.hpp"
+    m = re.search(r"kErfc%s\[(\d+)\]\s*=\s*\{([^}]*)\}" % which, text)
+    assert m, f"kErfc{which} not found in mx_ops.hpp"
     lits = [s.strip() for s in m.group(2).split(",")]
     assert len(lits) == int(m.group(1))
     return lits
 
 
-def test_header_constants_are_the_generated_fit():
+@pytest.mark.parametrize("which,bound", [("P", 2e-7), ("Q", 2e-8)])
+def test_header_constants_are_the_generated_fit(which, bound):
     gen = _gen()
-    assert header_coefficients() == gen.c_literals()
-    _, err = gen.fit()
-    assert err < 2e-7
+    assert header_coefficients(which) == gen.c_literals(which)
+    _, err = gen.fit(which)
+    assert err < bound
 
 
-def _emulate(coeffs, g):
-    """float32 steps of ActGelu: (act, derivative), each already rescaled."""
+def _emulate(which, g):
+    """float32 steps of ActGelu: (act, derivative), each already rescaled.
+    "P": the forward's act, t e^(-z^2 + P(x)) (its derivative is the same
+    cdf plus a separate Gaussian); "Q": the backward's act and derivative,
+    t e^(-z^2) Q(x) with e^(-z^2) shared with the Gaussian."""
     f32 = np.float32
-    c = [f32(float.fromhex(s.rstrip("f"))) for s in coeffs]
+    c = [f32(float.fromhex(s.rstrip("f"))) for s in header_coefficients(which)]
     l2e = f32(1.4426950408889634)
     with np.errstate(all="ignore"):
         far = g < f32(-8.0)
@@ -57,21 +62,25 @@ def _emulate(coeffs, g):
         p = np.full_like(x, c[-1])
         for ci in c[-2::-1]:
             p = (p * x + ci).astype(f32)
-        e = ((f32(-0.5) * g) * g + p).astype(f32)
-        q = (th * np.exp2((e * l2e + sc).astype(f32))).astype(f32)
-        cdf = np.where(g < 0, q, f32(1.0) - q).astype(f32)
         gauss = np.exp2((((f32(-0.5) * (g * g)) * l2e) + sc).astype(f32)).astype(f32)
+        if which == "P":
+            e = ((f32(-0.5) * g) * g + p).astype(f32)
+            q = (th * np.exp2((e * l2e + sc).astype(f32))).astype(f32)
+        else:
+            q = ((th * p).astype(f32) * gauss).astype(f32)
+        cdf = np.where(g < 0, q, f32(1.0) - q).astype(f32)
         act = (g * cdf).astype(np.float64)
         grad = (cdf + g * (f32(0.3989422804014327) * gauss)).astype(np.float64)
     scale = np.where(far, 2.0 ** -64, 1.0)
     return act * scale, grad * scale
 
 
-def test_float32_evaluation_error_over_every_bf16_gate():
+@pytest.mark.parametrize("which", ["P", "Q"])
+def test_float32_evaluation_error_over_every_bf16_gate(which):
     bits = np.arange(65536, dtype=np.uint32)
     g = (bits << 16).view(np.float32)
     g = g[np.isfinite(g)]
-    act, grad = _emulate(header_coefficients(), g)
+    act, grad = _emulate(which, g)
     gd = g.astype(np.float64)
     cdf = scipy_special.ndtr(gd)
     want_act = gd * cdf
@@ -86,3 +95,4 @@ def test_float32_evaluation_error_over_every_bf16_gate():
     err = np.abs(grad - want_grad) / np.maximum(np.abs(want_grad), 1e-3)
     ok = np.abs(want_grad) > 1e-37
     assert err[ok].max() < 1e-4, err[ok].max()
+    print(f"  {which}: act max rel error {rel.max():.2e}, derivative {err[ok].max():.2e}")
