@@ -16,9 +16,9 @@
 // of A (column l % 32 of B^T); its bytes 0..15 are elements 16 (l / 32) ..
 // +15 of the MFMA's first 32-element K block and bytes 16..31 the same
 // positions of its second block.  The scale of (row m, block b) comes from
-// lane m + 32 b (op_sel picks the register byte).  The 32x32 fp32 result
-// sits in 16 registers: lane l, register v holds row 8 (v / 4) + 4 (l / 32)
-// + v % 4, column l % 32.
+// lane m + 32 b (op_sel picks the register byte, 0 to 3).  The 32x32 fp32
+// result sits in 16 registers: lane l, register v holds row
+// 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
 //
 // Structure: a 256 x 256 C tile per 256-thread workgroup, one workgroup per
 // CU (148 KB of LDS); each wavefront owns 128 x 128 of C, its 256
@@ -158,9 +158,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
       ssb = u32x4_t{wb[0], wb[1], wb[2], wb[3]};
     }
   };
+  // Table row q keeps its 4 dwords rotated by (q / 16) % 4, so that 32
+  // consecutive rows read at one dword position hit 32 different banks.
+  auto rot = [](u32x4_t v, u32 k) {  // dword j moves to position (j + k) % 4
+    const u32 w0 = k == 0 ? v.x : k == 1 ? v.w : k == 2 ? v.z : v.y;
+    const u32 w1 = k == 0 ? v.y : k == 1 ? v.x : k == 2 ? v.w : v.z;
+    const u32 w2 = k == 0 ? v.z : k == 1 ? v.y : k == 2 ? v.x : v.w;
+    const u32 w3 = k == 0 ? v.w : k == 1 ? v.z : k == 2 ? v.y : v.x;
+    return u32x4_t{w0, w1, w2, w3};
+  };
   auto store_scales = [&](int buf) {
-    *reinterpret_cast<u32x4_t *>(&smemS[buf][t][0]) = ssa;
-    *reinterpret_cast<u32x4_t *>(&smemS[buf][kBM + t][0]) = ssb;
+    const u32 k = ((u32)t >> 4) & 3u;  // kBM is a multiple of 64: the same key for both halves
+    *reinterpret_cast<u32x4_t *>(&smemS[buf][t][0]) = rot(ssa, k);
+    *reinterpret_cast<u32x4_t *>(&smemS[buf][kBM + t][0]) = rot(ssb, k);
+  };
+  // this stage's 4 scale bytes of table row q, shifted so that the block of
+  // step s for this lane's half (block 2 s + h) is byte 2 s (op_sel 2 s)
+  auto read_scales = [&](int buf, u32 q, int in_grp_) {
+    const u32 pos = ((u32)in_grp_ + (q >> 4)) & 3u;
+    const u32 v = *reinterpret_cast<const u32 *>(&smemS[buf][q][4u * pos]);
+    return (int)(v >> (8u * (u32)h));
   };
   // ---- operands: global -> LDS directly (global_load_lds_dwordx4: lane
   // l's 16 bytes land at the instruction's LDS base + 16 l).  Wave w fills
@@ -211,8 +228,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     if (more_scales && in_grp == 0) load_scales(grp + 1);
     // this stage's operands and scales for both MFMA steps, all read before
     // the first MFMA in the order the MFMAs consume them; in step s lane
-    // r + 32 h takes block 4 in_grp + 2 s + h of its row in each 32-row tile
-    int csa[2][4], csb[2][4];
+    // r + 32 h takes block 4 in_grp + 2 s + h of its row in each 32-row
+    // tile, byte 2 s of the scale word (op_sel 2 s)
+    int csa[4], csb[4];
     v8i_t av[2][4], bv[2][4];
     auto read_op = [&](const uint8_t *base, u32 row, u32 s) {
       const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&base[lds_off(row, 4u * s + h)]);
@@ -220,11 +238,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
       return v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     };
 #pragma unroll
+    for (int i = 0; i < 4; i++) csa[i] = read_scales(grp & 1, (u32)(wm * 128 + 32 * i + r), in_grp);
+#pragma unroll
+    for (int j = 0; j < 4; j++) csb[j] = read_scales(grp & 1, (u32)(kBM + wn * 128 + 32 * j + r), in_grp);
+#pragma unroll
     for (int s = 0; s < 2; s++) {
-#pragma unroll
-      for (int i = 0; i < 4; i++) csa[s][i] = smemS[grp & 1][wm * 128 + 32 * i + r][4 * in_grp + 2 * s + h];
-#pragma unroll
-      for (int j = 0; j < 4; j++) csb[s][j] = smemS[grp & 1][kBM + wn * 128 + 32 * j + r][4 * in_grp + 2 * s + h];
       av[s][0] = read_op(smemA[buf], (u32)(wm * 128 + r), s);
 #pragma unroll
       for (int j = 0; j < 4; j++) bv[s][j] = read_op(smemB[buf], (u32)(wn * 128 + 32 * j + r), s);
@@ -244,14 +262,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[0][i], bv[0][j], acc[i][j], 0, 0, 0, csa[0][i],
-                                                                     0, csb[0][j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[0][i], bv[0][j], acc[i][j], 0, 0, 0, csa[i], 0,
+                                                                     csb[j]);
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[1][i], bv[1][j], acc[i][j], 0, 0, 0, csa[1][i],
-                                                                     0, csb[1][j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[1][i], bv[1][j], acc[i][j], 0, 0, 2, csa[i], 2,
+                                                                     csb[j]);
     __builtin_amdgcn_sched_barrier(0);
     // this wave's loads have landed; the barrier makes every wave's visible
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
