@@ -179,6 +179,43 @@ def test_gemm_16384x8192x5120_sampled(oracle_mod):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("scales", ["packed", "padded"])
+def test_gemm_ragged_16000x8000x5216_sampled(oracle_mod, scales):
+    """Full-size ragged shape: partial 256-row and 256-column tiles, a last
+    K stage of 96 columns, and 163 scale blocks per row (a partial last
+    scale group).  Packed scale rows (163 bytes apart) take the byte-wise
+    scale path; rows padded to 176 bytes take the 16-byte path for the full
+    groups and the byte-wise one for the last."""
+    dev = _dev()
+    M, N, K = 16000, 8000, 5216
+    print(f"case: gemm {M}x{N}x{K}, {scales} scales, sampled", flush=True)
+    x = synth.normal_bf16((M, K), 1.0, seed=62, device=dev)
+    w = synth.normal_bf16((N, K), 0.02, seed=63, device=dev)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(x, rowwise=True)
+    qb, _, sb, _ = mx.mxfp8_quant_2d(w, rowwise=True)
+    del x, w
+    if scales == "padded":
+        pa = torch.zeros((M, 176), dtype=torch.uint8, device=dev)
+        pb = torch.zeros((N, 176), dtype=torch.uint8, device=dev)
+        pa[:, :K // 32] = sa
+        pb[:, :K // 32] = sb
+        sa_in, sb_in = pa[:, :K // 32], pb[:, :K // 32]
+    else:
+        sa_in, sb_in = sa, sb
+    c = mx.mxfp8_gemm(qa, sa_in, qb, sb_in)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(10)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], rng.integers(0, M, 12)]))
+    cols = np.unique(np.concatenate([[0, 255, 256, N - 1], rng.integers(0, N, 28)]))
+    ridx = torch.from_numpy(rows).to(dev)
+    cidx = torch.from_numpy(cols).to(dev)
+    got = c[ridx][:, cidx].cpu().numpy()
+    _check(oracle_mod, f"ragged_{scales}", qa[ridx].cpu().numpy(), sa[ridx].cpu().numpy(), qb[cidx].cpu().numpy(),
+           sb[cidx].cpu().numpy(), got)
+    del qa, qb, sa, sb, c
+    torch.cuda.empty_cache()
+
+
 def test_gemm_single_products_exact_and_truncation_threshold():
     """The two facts the bound rests on.  With one nonzero per row (K = 32),
     C[m][n] is one product: exact for all 65536 code pairs, NaN exactly
