@@ -15,6 +15,13 @@ timing on the launch stream), `cpu_baseline` (the CPU oracle on a bounded
 sample of the same workload), `detail` (each op and layout alone, the other
 gated activations, the MX GEMM consumer against the fp8 MFMA peak, the 3D
 expert cast, a copy-kernel ceiling).
+
+`--sweep` prints instead a markdown table over the pages' shapes: every
+direction and layout, fused and unfused (the activation written as bf16,
+then the plain cast), with the pages' columns ("Add swiglu + MXFP8 fused
+CuTe DSL kernel", Performance), and the 3D expert cast over 1 to 64 experts
+of 8192 x 5120 ("[mxfp8 moe training] update 3d quant colwise scaling
+kernel to use single input/output TMA descriptors", Performance).
 """
 from __future__ import annotations
 
@@ -42,6 +49,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-detail", action="store_true", help="skip the per-op breakdown")
     p.add_argument("--validate", action="store_true", help="check sampled outputs against the oracle before timing")
+    p.add_argument("--sweep", action="store_true", help="print the per-shape table instead of the JSON line")
     return p.parse_args()
 
 
@@ -169,12 +177,78 @@ def validate(inp):
     print("validate: sampled slabs match the oracle", file=sys.stderr, flush=True)
 
 
+SWEEP_SHAPES = ((128, 128), (4096, 2048), (4096, 7168), (16384, 7168), (131072, 8192))
+SWEEP_EXPERTS = (1, 2, 4, 8, 16, 32, 64)
+
+
+def run_sweep():
+    """The pages' table on MI355X: fused and unfused time, speedup and
+    achieved HBM GB/s for every shape, direction and layout; then the 3D
+    expert cast.  Inputs: gate/up the halves of one N(0, 1) bf16 w13 tensor,
+    dh N(0, 1); experts N(0, 0.02)."""
+    import torch
+
+    import swiglu_activation_cast_amd as mx
+    from swiglu_activation_cast_amd import metrics, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    print("| input_shape (M, K) | direction | scales | unfused µs | fused µs | speedup | fused GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|---|---|---|---|")
+    for M, N in SWEEP_SHAPES:
+        inp = synth.swiglu_inputs(M, N, seed=5, std=1.0, packed=True, device=dev)
+        outs = {"forward": mx.alloc_outputs(M, N, mx.BOTH, dev), "backward": mx.alloc_outputs(M, 2 * N, mx.BOTH, dev)}
+        vals = {"forward": torch.empty((M, N), dtype=torch.bfloat16, device=dev),
+                "backward": torch.empty((M, 2 * N), dtype=torch.bfloat16, device=dev)}
+        for direction in ("forward", "backward"):
+            out, v = outs[direction], vals[direction]
+            for lay, lname in ((mx.ROWWISE, "rowwise"), (mx.COLWISE, "colwise"), (mx.BOTH, "both")):
+                fl = dict(rowwise=bool(lay & 1), colwise=bool(lay & 2))
+                if direction == "forward":
+                    fused = lambda: mx.mxfp8_swiglu_fwd(inp.gate, inp.up, out=out, stream=stream, **fl)
+
+                    def unfused():
+                        mx.mxfp8_swiglu_fwd_bf16(inp.gate, inp.up, out=v, stream=stream)
+                        mx.mxfp8_quant_2d(v, out=out, stream=stream, **fl)
+                    nbytes = metrics.swiglu_fwd_bytes(M, N, lay)
+                else:
+                    fused = lambda: mx.mxfp8_swiglu_bwd(inp.dh, inp.gate, inp.up, out=out, stream=stream, **fl)
+
+                    def unfused():
+                        mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up, out=v, stream=stream)
+                        mx.mxfp8_quant_2d(v, out=out, stream=stream, **fl)
+                    nbytes = metrics.swiglu_bwd_bytes(M, N, lay)
+                tu, _ = time_launches(unfused, 20, 10)
+                tf, _ = time_launches(fused, 20, 10)
+                gbps = metrics.gbps(nbytes, tf)
+                print(f"| ({M}, {N}) | {direction} | {lname} | {tu * 1e6:.2f} | {tf * 1e6:.2f} | {tu / tf:.2f}× | "
+                      f"{gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% |", flush=True)
+        del inp, outs, vals
+        torch.cuda.empty_cache()
+    print()
+    print("| experts (E, 8192, 5120) | 3D colwise µs | GB/s | % of 8 TB/s |")
+    print("|---|---|---|---|")
+    for E in SWEEP_EXPERTS:
+        w = synth.expert_weights(E, 8192, 5120, seed=3 + E, device=dev)
+        q = torch.empty((E, 5120, 8192), dtype=torch.uint8, device=dev)
+        sc = torch.empty((E, 5120, 256), dtype=torch.uint8, device=dev)
+        t, _ = time_launches(lambda: mx.mxfp8_quant_3d_colwise(w, out=(q, sc), stream=stream), 20, 10)
+        gbps = metrics.gbps(metrics.quant_3d_bytes(E, 8192, 5120), t)
+        print(f"| ({E}, 8192, 5120) | {t * 1e6:.2f} | {gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% |", flush=True)
+        del w, q, sc
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the cast shards rows or experts "
               "across GPUs with no exchange, so the one-GPU number is the per-GPU figure.", file=sys.stderr)
         sys.exit(2)
+    if args.sweep:
+        run_sweep()
+        return
 
     import torch
 
