@@ -126,19 +126,33 @@ def alloc_outputs(M: int, W: int, layout: int, device) -> Tuple[torch.Tensor, ..
     return q_row, q_col, s_row, s_col
 
 
-def _out_args(outs: Sequence[torch.Tensor], layout: int):
+def _out_args(outs: Sequence[torch.Tensor], layout: int, M: int, W: int, device):
+    """(pointer, leading dimension) pairs of the four outputs of an [M, W]
+    result.  The C ABI cannot see buffer sizes, so every enabled output is
+    checked here against its full extent: q_row [M, W], s_row [M, W/32],
+    q_col [W, M], s_col [W, M/32], uint8, on the inputs' device, unit column
+    stride (a larger row stride is allowed)."""
+    if len(outs) != 4:
+        raise ValueError("out must be (q_row, q_col, s_row, s_col)")
     q_row, q_col, s_row, s_col = outs
+    device = torch.device(device)
 
-    def mat(t, on):
+    def mat(t, on, name, rows, cols):
         if not on:
             return [None, 0]
-        if t.dtype != torch.uint8 or not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
-            raise ValueError("outputs must be 2-D uint8 GPU tensors with unit column stride")
-        return [t.data_ptr(), t.stride(0)]
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D uint8 tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
+        if tuple(t.shape) != (rows, cols):
+            raise ValueError(f"{name} must have shape {(rows, cols)}, got {tuple(t.shape)}")
+        if cols > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} must have unit column stride")
+        return [t.data_ptr(), t.stride(0) if rows > 1 else max(t.stride(0), cols)]
 
-    return mat(q_row, layout & ROWWISE) + mat(s_row, layout & ROWWISE) + mat(q_col, layout & COLWISE) + mat(
-        s_col, layout & COLWISE
-    )
+    rows, cols = layout & ROWWISE, layout & COLWISE
+    return (mat(q_row, rows, "q_row", M, W) + mat(s_row, rows, "s_row", M, W // 32)
+            + mat(q_col, cols, "q_col", W, M) + mat(s_col, cols, "s_col", W, M // 32))
 
 
 def mxfp8_swiglu_fwd(gate: torch.Tensor, up: torch.Tensor, *, rowwise: bool = True, colwise: bool = False,
@@ -151,7 +165,7 @@ def mxfp8_swiglu_fwd(gate: torch.Tensor, up: torch.Tensor, *, rowwise: bool = Tr
         raise ValueError("gate and up must have the same shape and device")
     M, N = gate.shape
     outs = out if out is not None else alloc_outputs(M, N, layout, gate.device)
-    st = lib().mxfp8_swiglu_fwd(pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+    st = lib().mxfp8_swiglu_fwd(pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout, M, N, gate.device),
                                 _stream(gate.device, stream))
     _check("mxfp8_swiglu_fwd", st)
     return tuple(outs)
@@ -168,7 +182,7 @@ def mxfp8_swiglu_bwd(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, *, 
         raise ValueError("dh, gate and up must have the same shape and device")
     M, N = gate.shape
     outs = out if out is not None else alloc_outputs(M, 2 * N, layout, gate.device)
-    st = lib().mxfp8_swiglu_bwd(pd, ldd, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+    st = lib().mxfp8_swiglu_bwd(pd, ldd, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout, M, 2 * N, gate.device),
                                 _stream(gate.device, stream))
     _check("mxfp8_swiglu_bwd", st)
     return tuple(outs)
@@ -194,7 +208,7 @@ def mxfp8_gated_fwd(gate: torch.Tensor, up: torch.Tensor, *, act="silu", rowwise
         raise ValueError("gate and up must have the same shape and device")
     M, N = gate.shape
     outs = out if out is not None else alloc_outputs(M, N, layout, gate.device)
-    st = lib().mxfp8_gated_fwd(code, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+    st = lib().mxfp8_gated_fwd(code, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout, M, N, gate.device),
                                _stream(gate.device, stream))
     _check("mxfp8_gated_fwd", st)
     return tuple(outs)
@@ -212,7 +226,7 @@ def mxfp8_gated_bwd(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, *, a
         raise ValueError("dh, gate and up must have the same shape and device")
     M, N = gate.shape
     outs = out if out is not None else alloc_outputs(M, 2 * N, layout, gate.device)
-    st = lib().mxfp8_gated_bwd(code, pd, ldd, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout),
+    st = lib().mxfp8_gated_bwd(code, pd, ldd, pg, ldg, pu, ldu, M, N, layout, *_out_args(outs, layout, M, 2 * N, gate.device),
                                _stream(gate.device, stream))
     _check("mxfp8_gated_bwd", st)
     return tuple(outs)
@@ -225,7 +239,7 @@ def mxfp8_quant_2d(x: torch.Tensor, *, rowwise: bool = True, colwise: bool = Fal
     px, ldx = _bf16_matrix(x, "x")
     M, K = x.shape
     outs = out if out is not None else alloc_outputs(M, K, layout, x.device)
-    st = lib().mxfp8_quant_2d(px, ldx, M, K, layout, *_out_args(outs, layout), _stream(x.device, stream))
+    st = lib().mxfp8_quant_2d(px, ldx, M, K, layout, *_out_args(outs, layout, M, K, x.device), _stream(x.device, stream))
     _check("mxfp8_quant_2d", st)
     return tuple(outs)
 
