@@ -1,4 +1,6 @@
-"""Comparison of GPU outputs with the oracle's, block by block.
+"""Comparison of GPU outputs with the oracle's, block by block -- TEST
+INFRASTRUCTURE ONLY (used by the tests, the smoke check and the benchmark's
+validation before timing; never by the product path).
 
 Quant-only casts must match bit for bit.  The fused casts compute their
 activation in fp32 with hardware exp2/reciprocal, so a value may land one
@@ -20,7 +22,13 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from helpers import e4m3_ordinal
+
+
+def e4m3_ordinal(codes: np.ndarray) -> np.ndarray:
+    """Signed position of an E4M3 code on the number line (+0 and -0 both 0)."""
+    c = np.asarray(codes).astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
 
 
 @dataclass
@@ -34,6 +42,21 @@ class Stats:
     def merge(self, o: "Stats") -> "Stats":
         return Stats(self.blocks + o.blocks, self.scale_mismatch + o.scale_mismatch,
                      self.code_off_by_one + o.code_off_by_one, self.elements + o.elements, self.notes + o.notes)
+
+    @property
+    def scale_mismatch_rate(self) -> float:
+        """Blocks whose scale differs from the oracle's, over all blocks."""
+        return self.scale_mismatch / max(1, self.blocks)
+
+    @property
+    def one_code_rate(self) -> float:
+        """Elements one E4M3 step from the oracle's code, over all elements."""
+        return self.code_off_by_one / max(1, self.elements)
+
+    def record(self) -> dict:
+        return {"blocks": self.blocks, "scale_mismatch": self.scale_mismatch,
+                "scale_mismatch_rate": self.scale_mismatch_rate, "elements": self.elements,
+                "one_code": self.code_off_by_one, "one_code_rate": self.one_code_rate}
 
 
 def assert_exact(name, got, want):
@@ -106,14 +129,29 @@ def colwise_view(q, s, values):
 
 
 def compare_fused(oracle, name, gpu, orc, values, layout) -> Stats:
-    """gpu / orc: (q_row, s_row, q_col, s_col) numpy tuples; values: [M, W] bf16 bits."""
+    """gpu / orc: (q_row, s_row, q_col, s_col) numpy tuples; values: [M, W] bf16 bits.
+    The returned Stats covers every enabled layout; ``.notes`` holds the
+    per-layout Stats as ("row" | "col", Stats) pairs."""
     st = Stats()
     if layout & 1:
-        st = st.merge(compare_blocks(oracle, name + "/row", *rowwise_view(gpu[0], gpu[1], values)[:2],
-                                     *rowwise_view(orc[0], orc[1], values)))
+        part = compare_blocks(oracle, name + "/row", *rowwise_view(gpu[0], gpu[1], values)[:2],
+                              *rowwise_view(orc[0], orc[1], values))
+        st = st.merge(part)
+        st.notes.append(("row", part))
     if layout & 2:
-        st = st.merge(compare_blocks(oracle, name + "/col", *colwise_view(gpu[2], gpu[3], values)[:2],
-                                     *colwise_view(orc[2], orc[3], values)))
+        part = compare_blocks(oracle, name + "/col", *colwise_view(gpu[2], gpu[3], values)[:2],
+                              *colwise_view(orc[2], orc[3], values))
+        st = st.merge(part)
+        st.notes.append(("col", part))
     rate = st.code_off_by_one / max(1, st.elements)
     assert rate <= 1e-3, f"{name}: one-step code differences on {rate:.2e} of elements"
     return st
+
+
+def layout_parts(st: Stats) -> dict:
+    """{"row" | "col": Stats} of a compare_fused result (merged when the
+    result itself merges several comparisons)."""
+    out = {}
+    for lay, part in st.notes:
+        out[lay] = out[lay].merge(part) if lay in out else part
+    return out

@@ -1,4 +1,6 @@
-"""Compiles the gfx950 HIP library (libmxfp8.so) in-tree with hipcc."""
+"""Compiles the gfx950 HIP libraries in-tree with hipcc: libmxfp8.so (the
+casts and their consumer, behind include/mxfp8.h) and libmxstream.so (the
+streaming bandwidth probe behind include/mxstream.h, measurement only)."""
 from __future__ import annotations
 
 import hashlib
@@ -12,6 +14,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libmxfp8.so")
 SOURCES = [os.path.join(CSRC, "mxfp8.hip")]
+STREAM_LIB_PATH = os.path.join(PKG_DIR, "libmxstream.so")
+STREAM_SOURCES = [os.path.join(CSRC, "mx_stream.hip")]
 ARCH = "gfx950"
 
 
@@ -48,9 +52,10 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bool = False) -> str:
+def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bool = False,
+          sources: list[str] | None = None) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *compile_flags(), *(extra_flags or []), "-shared", "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *compile_flags(), *(extra_flags or []), "-shared", "-o", tmp, *(sources or SOURCES)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -65,5 +70,10 @@ def build(out: str = LIB_PATH, extra_flags: list[str] | None = None, verbose: bo
     return out
 
 
+def build_all(verbose: bool = False) -> None:
+    build(verbose=verbose)
+    build(STREAM_LIB_PATH, verbose=verbose, sources=STREAM_SOURCES)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    build_all(verbose=True)

@@ -2,20 +2,25 @@
 
 Three subcommands, each writing one summary file:
 
-  stats    <kernel_stats.csv>            from `rocprofv3 --kernel-trace --stats`
+  stats    <kernel_trace.csv>            from `rocprofv3 --kernel-trace`: the
+                                         duration of every bench call, each
+                                         call keyed by its kernel and grid
   traffic  <fetch_dir> <write_dir>       from two `rocprofv3 --pmc` runs, one
                                          with FETCH_SIZE, one with WRITE_SIZE
   counters <dir> [<dir> ...]             any `rocprofv3 --pmc` runs: the mean
                                          per dispatch of every counter for the
-                                         kernels matching --kernel
+                                         kernels matching --kernel (and --grid)
+
+The bench launches some kernels for several calls (the plain colwise cast
+for the 2D cast and for the 64-expert 3D cast, the both-layout cast for each
+unfused pipeline); their grids differ, so every summary keys a dispatch by
+(kernel name, grid size) and labels it with the bench call of that shape.
 
 Counter values are KiB per dispatch as the L2 reports them.  They are
-calibrated on the bench's device copy of the w13 tensor (a copy kernel of
-known size: every byte read once and written once), so that "calibrated
-bytes" means bytes moved to or from HBM as that copy counts them.  Each
-dispatch group (kernel name, read volume) is matched to the bench call it
-comes from by its kernel and its calibrated read bytes, which equal the
-call's algorithmic read bytes when nothing is re-read.
+calibrated on the streaming probe's copies (libmxstream.so, one input and one
+output buffer of 1 GiB: every byte read once and written once, with the same
+nontemporal accesses as the casts), so that "calibrated bytes" means bytes
+moved to or from HBM as that copy counts them.
 """
 from __future__ import annotations
 
@@ -24,40 +29,83 @@ import collections
 import csv
 import os
 import re
+import statistics
+from dataclasses import dataclass
 
 from . import _build, metrics, synth
 
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_KERNEL = "k_stream<1, 1,"
+COPY_BYTES = 1 << 30  # the probe's buffers (bench.py stream_ceilings)
+THREADS = 256  # work-items per workgroup of every kernel the bench times
+
+
+@dataclass
+class Call:
+    pattern: str  # substring of the kernel name
+    label: str
+    read: int  # algorithmic bytes per launch
+    write: int
+    grid: int  # workgroups
+
+
+def _tiles(M, N, E=1):
+    return -(-M // 128) * -(-N // 128) * E
 
 
 def bench_calls(workload: str, experts: int):
-    """(kernel pattern, label, algorithmic read bytes, algorithmic write bytes)
-    for every kernel the bench launches."""
+    """Every kernel call the bench times, with its algorithmic bytes and grid."""
     cfg = synth.WORKLOADS[workload]
     M, N = cfg["M"], cfg["N"]
     ex = synth.EXPERT_WORKLOADS[experts]
     E, N3, K3 = ex["E"], ex["N"], ex["K"]
     one = M * N + M * N // 32  # one cast layout of an [M, N] result
-
-    def split(total, read):
-        return read, total - read
+    rows = -(-M // 4)  # rowwise kernels: four rows per workgroup
 
     calls = []
-    for lay, name, rows_arg in ((1, "row", None), (2, "col", "false"), (3, "both", "true")):
+    for lay, name in ((1, "row"), (2, "col"), (3, "both")):
         for op, fn, rd in (("Fwd", metrics.swiglu_fwd_bytes, 4 * M * N), ("Bwd", metrics.swiglu_bwd_bytes, 6 * M * N)):
-            pat = f"k_rowwise<mx::Op{op}," if rows_arg is None else f"k_tiled<mx::Op{op}, {rows_arg}>"
-            calls.append((pat, f"{op.lower()}_{name}", *split(fn(M, N, lay), rd)))
+            if lay == 1:
+                pat, grid = f"k_rowwise<mx::Op{op},", rows
+            else:
+                pat, grid = f"k_tiled<mx::Op{op}, {'true' if lay == 3 else 'false'}>", _tiles(M, N)
+            calls.append(Call(pat, f"{op.lower()}_{name}", rd, fn(M, N, lay) - rd, grid))
+    for act in ("GeluTanh", "Gelu", "Relu"):
+        label = {"GeluTanh": "gelu_tanh", "Gelu": "gelu", "Relu": "relu"}[act]
+        for op, fn, rd in (("Fwd", metrics.swiglu_fwd_bytes, 4 * M * N), ("Bwd", metrics.swiglu_bwd_bytes, 6 * M * N)):
+            calls.append(Call(f"k_tiled<mx::Gated{op}<mx::Act{act}>, true>", f"{label}_{op.lower()}_both", rd,
+                              fn(M, N, 3) - rd, _tiles(M, N)))
     calls += [
-        ("k_rowwise<mx::OpQuant,", "quant2d_row", *split(metrics.quant_2d_bytes(M, N, 1), 2 * M * N)),
-        ("k_tiled<mx::OpQuant, false>", "quant2d_col", *split(metrics.quant_2d_bytes(M, N, 2), 2 * M * N)),
-        ("k_tiled<mx::OpQuant, false>", f"quant3d_E{E}", *split(metrics.quant_3d_bytes(E, N3, K3), 2 * E * N3 * K3)),
-        ("k_values<mx::OpFwd,", "unfused_fwd_values", 4 * M * N, 2 * M * N),
-        ("k_values<mx::OpBwd,", "unfused_bwd_values", 6 * M * N, 4 * M * N),
-        ("k_tiled<mx::OpQuant, true>", "unfused_fwd_quant_both", 2 * M * N, 2 * one),
-        ("k_tiled<mx::OpQuant, true>", "unfused_bwd_quant_both", 4 * M * N, 4 * one),
+        Call("k_rowwise<mx::OpQuant,", "quant2d_row", 2 * M * N, one, rows),
+        Call("k_tiled<mx::OpQuant, false>", "quant2d_col", 2 * M * N, one, _tiles(M, N)),
+        Call("k_tiled<mx::OpQuant, false>", f"quant3d_E{E}", 2 * E * N3 * K3,
+             metrics.quant_3d_bytes(E, N3, K3) - 2 * E * N3 * K3, _tiles(N3, K3, E)),
+        Call("k_values<mx::OpFwd,", "unfused_fwd_values", 4 * M * N, 2 * M * N, rows),
+        Call("k_values<mx::OpBwd,", "unfused_bwd_values", 6 * M * N, 4 * M * N, rows),
+        Call("k_tiled<mx::OpQuant, true>", "unfused_fwd_quant_both", 2 * M * N, 2 * one, _tiles(M, N)),
+        Call("k_tiled<mx::OpQuant, true>", "unfused_bwd_quant_both", 4 * M * N, 4 * one, _tiles(M, 2 * N)),
     ]
-    copy_bytes = M * 2 * N * 2  # the w13 tensor [M, 2N] bf16
-    return calls, copy_bytes
+    gib = COPY_BYTES
+    for mix, (nr, nw) in (("4:1", (4, 1)), ("2:1", (2, 1)), ("3:1", (3, 1)), ("3:2", (3, 2)), ("1:1", (1, 1))):
+        for u in (4, 8):
+            for grid in (2048, 4096, 8192):
+                calls.append(Call(f"k_stream<{nr}, {nw}, {u}>", f"stream_{mix}_u{u}_g{grid}", nr * gib, nw * gib,
+                                  grid))
+    return calls
+
+
+def _match(calls, kernel: str, grid_items: int):
+    """The bench call a dispatch of `kernel` with `grid_items` work-items
+    belongs to (None if it is not one of them)."""
+    for c in calls:
+        if c.pattern in kernel and c.grid * THREADS == grid_items:
+            return c
+    return None
+
+
+def _short(kernel: str) -> str:
+    """Kernel name without return type, parameters or spaces (one column)."""
+    name = re.sub(r"^void |\(.*$", "", kernel.replace("(anonymous namespace)::", ""))
+    return name.replace(", ", ",")
 
 
 def _counter_rows(d: str):
@@ -67,75 +115,60 @@ def _counter_rows(d: str):
 
 
 def _per_dispatch(rows, counter):
-    """{dispatch id: (kernel name, value)} for one counter."""
+    """{dispatch id: (kernel name, grid work-items, value)} for one counter."""
     out = {}
     for r in rows:
         if r["Counter_Name"] == counter:
-            out[r["Dispatch_Id"]] = (r["Kernel_Name"], float(r["Counter_Value"]))
+            out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"]))
     return out
 
 
-def _groups(values):
-    """Group (kernel, KiB) samples by kernel and by value within 1 %."""
-    groups = collections.defaultdict(list)
-    for kernel, v in values:
-        for key in groups:
-            if key[0] == kernel and abs(key[1] - v) <= 0.01 * max(key[1], 1.0):
-                groups[key].append(v)
-                break
-        else:
-            groups[(kernel, v)].append(v)
-    return {(k, sum(v) / len(v)): len(v) for (k, _), v in groups.items()}
-
-
-def _calibration(samples, copy_bytes):
-    """Factor that turns counted bytes (KiB x 1024) into copied bytes, from the
-    copy dispatches of copy_bytes."""
-    vals = [v for k, v in samples if COPY_KERNEL in k]
+def _calibration(samples):
+    """Factor that turns counted bytes (KiB x 1024) into bytes moved, from
+    the probe's copies of COPY_BYTES (every byte read once, written once)."""
+    vals = [v for k, _, v in samples if COPY_KERNEL in k]
     if not vals:
-        raise SystemExit(f"no {COPY_KERNEL} dispatch in the counter output")
-    top = max(vals)
-    big = [v for v in vals if v >= 0.99 * top]
-    kib = sum(big) / len(big)
-    return copy_bytes / (kib * 1024.0), kib
+        raise SystemExit(f"no {COPY_KERNEL} dispatch (the probe's copy) in the counter output")
+    kib = statistics.median(vals)
+    return COPY_BYTES / (kib * 1024.0), kib
 
 
 def traffic(fetch_dir, write_dir, workload, experts, command, out, kernel="bwd_both"):
-    calls, copy_bytes = bench_calls(workload, experts)
+    calls = bench_calls(workload, experts)
     fetch = _per_dispatch(_counter_rows(fetch_dir), "FETCH_SIZE")
     write = _per_dispatch(_counter_rows(write_dir), "WRITE_SIZE")
-    f_fac, f_kib = _calibration(fetch.values(), copy_bytes)
-    w_fac, w_kib = _calibration(write.values(), copy_bytes)
+    f_fac, f_kib = _calibration(fetch.values())
+    w_fac, w_kib = _calibration(write.values())
     lines = [
         f"# rocprofv3 HBM counter summary of bench.py ({workload}, 3D experts E={experts})",
         "# commands (one counter per run):",
         *[f"#   {c}" for c in command],
-        f"# calibration: the bench's device copy of the w13 tensor ({COPY_KERNEL}, {copy_bytes} bytes read and written)",
+        f"# calibration: the streaming probe's copies ({COPY_KERNEL}...>, {COPY_BYTES} bytes read and written)",
         f"#   FETCH_SIZE reads {f_kib:.0f} KiB -> factor {f_fac:.4f}; WRITE_SIZE reads {w_kib:.0f} KiB -> factor {w_fac:.4f}",
-        "# columns: call, kernel, dispatches, FETCH_SIZE KiB (avg), WRITE_SIZE KiB (avg),",
+        "# columns: call, kernel, grid (workgroups), dispatches, FETCH_SIZE KiB (avg), WRITE_SIZE KiB (avg),",
         "#          calibrated HBM read / write GB, algorithmic read / write GB, excess",
         "",
     ]
-    fg = _groups(fetch.values())
-    # WRITE samples of the dispatches in each FETCH group (same dispatch order
-    # in both runs: the bench is deterministic)
-    f_list = sorted(fetch.items(), key=lambda kv: int(kv[0]))
-    w_list = sorted(write.items(), key=lambda kv: int(kv[0]))
-    if [k for _, (k, _) in f_list] != [k for _, (k, _) in w_list]:
-        raise SystemExit("the two counter runs launched different kernel sequences")
+    groups = collections.defaultdict(lambda: ([], []))
+    for did, (k, grid, v) in fetch.items():
+        c = _match(calls, k, grid)
+        if c is not None and not c.label.startswith("stream_"):
+            groups[c.label][0].append(v)
+    for did, (k, grid, v) in write.items():
+        c = _match(calls, k, grid)
+        if c is not None and not c.label.startswith("stream_"):
+            groups[c.label][1].append(v)
     machine = {}
-    for (kname, f_avg), n in sorted(fg.items(), key=lambda kv: -kv[0][1]):
-        match = [c for c in calls if c[0] in kname and abs(c[2] - f_avg * 1024 * f_fac) <= 0.01 * c[2]]
-        if not match:
+    by_label = {c.label: c for c in calls}
+    for label, (fv, wv) in sorted(groups.items(), key=lambda kv: -(by_label[kv[0]].read + by_label[kv[0]].write)):
+        if not fv or not wv:
             continue
-        pat, label, rd, wr = match[0]
-        ws = [w_list[i][1][1] for i, (_, (k, v)) in enumerate(f_list)
-              if k == kname and abs(v - f_avg) <= 0.01 * f_avg]
-        w_avg = sum(ws) / len(ws)
+        c = by_label[label]
+        f_avg, w_avg = sum(fv) / len(fv), sum(wv) / len(wv)
         hr, hw = f_avg * 1024 * f_fac, w_avg * 1024 * w_fac
-        short = re.sub(r"^void |\(.*$", "", kname)
-        lines.append(f"{label:24s} {short:30s} {n:4d} {f_avg:12.0f} {w_avg:12.0f}  hbm {hr / 1e9:.4f} / {hw / 1e9:.4f}"
-                     f"  alg {rd / 1e9:.4f} / {wr / 1e9:.4f}  (read {100 * (hr / rd - 1):+.2f}%, write {100 * (hw / wr - 1):+.2f}%)")
+        lines.append(f"{label:24s} {_short(c.pattern):34s} {c.grid:7d} {len(fv):4d} {f_avg:12.0f} {w_avg:12.0f}"
+                     f"  hbm {hr / 1e9:.4f} / {hw / 1e9:.4f}  alg {c.read / 1e9:.4f} / {c.write / 1e9:.4f}"
+                     f"  (read {100 * (hr / c.read - 1):+.2f}%, write {100 * (hw / c.write - 1):+.2f}%)")
         machine[label] = (round(hr), round(hw))
     if kernel not in machine:
         raise SystemExit(f"no dispatch of the {kernel} call found")
@@ -153,26 +186,49 @@ def traffic(fetch_dir, write_dir, workload, experts, command, out, kernel="bwd_b
         f.write("\n".join(lines) + "\n")
 
 
-def stats(csv_path, workload, experts, command, out, top=24):
+def stats(csv_path, workload, experts, command, out, top_other=6):
+    """Per-call kernel durations from a kernel_trace.csv: every dispatch is
+    keyed by (kernel, grid) and labelled with its bench call; the algorithmic
+    GB/s of the call follows from its average duration."""
+    calls = bench_calls(workload, experts)
     with open(csv_path) as f:
         rows = list(csv.DictReader(f))
-    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    durs = collections.defaultdict(list)
+    for r in rows:
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+        durs[(r["Kernel_Name"], int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1) or 1))].append(d)
     lines = [
-        f"# rocprofv3 kernel-trace summary of bench.py ({workload}, 3D experts E={experts})",
+        f"# rocprofv3 kernel-trace summary of bench.py ({workload}, 3D experts E={experts}), one row per bench call",
         *[f"# command: {c}" for c in command],
         f"# kernel source hash (bench.py kernel_source_hash): {_build.kernel_source_hash()}",
-        "# columns: calls, avg us, min us, max us, share of GPU time, kernel",
+        "# columns: call, kernel, grid (workgroups), dispatches, avg / median / min / max us,",
+        "#          algorithmic GB/s at the average, % of 8 TB/s",
         "",
     ]
-    for r in rows[:top]:
-        lines.append("%6s %10.1f %10.1f %10.1f %6.2f%%  %s" % (
-            r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
-            float(r["Percentage"]), r["Name"][:100]))
+    other = []
+    labelled = []
+    for (kernel, grid), d in durs.items():
+        c = _match(calls, kernel, grid)
+        if c is None:
+            other.append((sum(d), kernel, grid, d))
+            continue
+        avg = sum(d) / len(d)
+        gbps = metrics.gbps(c.read + c.write, avg * 1e-6)
+        labelled.append((c.label, _short(kernel), grid // THREADS, len(d), avg, statistics.median(d), min(d), max(d),
+                         gbps))
+    order = {c.label: i for i, c in enumerate(calls)}
+    for row in sorted(labelled, key=lambda r: order[r[0]]):
+        lines.append("%-24s %-34s %7d %4d %9.1f %9.1f %9.1f %9.1f %8.1f %6.2f%%" % (
+            *row, 100 * row[-1] / metrics.HBM_PEAK_GBPS))
+    if other:
+        lines += ["", "# other kernels (not a bench call), by total time: dispatches, avg us, kernel"]
+        for tot, kernel, grid, d in sorted(other, reverse=True)[:top_other]:
+            lines.append("# %5d %9.1f  %s" % (len(d), tot / len(d), _short(kernel)[:90]))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
-def counters(dirs, pattern, command, out, simds=1024, xcds=8):
+def counters(dirs, pattern, command, out, simds=1024, xcds=8, grid=None):
     """Mean per dispatch of each counter over dispatches whose kernel name
     contains `pattern`, plus two derived figures when their counters are
     present: matrix-core utilization (MFMA busy cycles over active cycles
@@ -182,14 +238,15 @@ def counters(dirs, pattern, command, out, simds=1024, xcds=8):
     names = set()
     for d in dirs:
         for r in _counter_rows(d):
-            if pattern in r["Kernel_Name"]:
+            if pattern in r["Kernel_Name"] and (grid is None or int(r["Grid_Size"]) == grid * THREADS):
                 vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
                 names.add(re.sub(r"^void |\(.*$", "", r["Kernel_Name"]))
     if not vals:
         raise SystemExit(f"no dispatch of a kernel matching {pattern!r}")
     mean = {k: sum(v) / len(v) for k, v in vals.items()}
     lines = [
-        f"# rocprofv3 counter summary: kernels matching {pattern!r} ({', '.join(sorted(names))})",
+        f"# rocprofv3 counter summary: kernels matching {pattern!r} ({', '.join(sorted(names))})"
+        + (f", grid {grid} workgroups" if grid else ""),
         *[f"# command: {c}" for c in command],
         f"# kernel source hash (bench.py kernel_source_hash): {_build.kernel_source_hash()}",
         "# columns: counter, mean per dispatch, dispatches",
@@ -225,13 +282,14 @@ def main(argv=None):
     c = sub.add_parser("counters")
     c.add_argument("dirs", nargs="+")
     c.add_argument("--kernel", required=True, help="substring of the kernel name")
+    c.add_argument("--grid", type=int, default=None, help="only dispatches of this many workgroups")
     a = p.parse_args(argv)
     if a.kind == "stats":
         stats(a.csv, a.workload, a.experts, a.command, a.out)
     elif a.kind == "traffic":
         traffic(a.fetch_dir, a.write_dir, a.workload, a.experts, a.command, a.out)
     else:
-        counters(a.dirs, a.kernel, a.command, a.out)
+        counters(a.dirs, a.kernel, a.command, a.out, grid=a.grid)
 
 
 if __name__ == "__main__":

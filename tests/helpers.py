@@ -25,3 +25,18 @@ def e4m3_ordinal(codes: np.ndarray) -> np.ndarray:
     c = codes.astype(np.int32)
     mag = c & 0x7F
     return np.where(c & 0x80, -mag, mag)
+
+
+# ------------------------------------------------------------ parity rates
+# (config, direction, layout) -> merged oracle.parity.Stats of every fused
+# comparison recorded in this session; printed at the end of the run (and
+# written as JSON to $MXFP8_PARITY_RATES when that is set) by conftest.py.
+PARITY_RATES = {}
+
+
+def record_rates(config: str, direction: str, st) -> None:
+    from oracle.parity import layout_parts
+
+    for lay, part in layout_parts(st).items():
+        key = (config, direction, lay)
+        PARITY_RATES[key] = PARITY_RATES[key].merge(part) if key in PARITY_RATES else part

@@ -294,3 +294,24 @@ def test_grouped_gemm_errors():
     assert ggemm(offs=A + 2) == ALIGN
     assert ggemm(lda=120) == STRIDE
     assert ggemm(M=0, a=None) == OK
+
+
+def test_stream_probe_exports_and_checks():
+    """libmxstream.so (the bandwidth probe) exports what include/mxstream.h
+    declares and rejects bad arguments before any launch."""
+    from swiglu_activation_cast_amd import stream_probe
+
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "mxstream.h")).read(), flags=re.S)
+    names = set(re.findall(r"\b(mxstream_\w+)\s*\(", text))
+    assert names == {"mxstream_mix"}
+    lib = stream_probe.lib()
+    bufs = (ctypes.c_void_p * 4)(A, A + 4096, A + 8192, A + 12288)
+    assert lib.mxstream_mix(None, 1, bufs, 1, 32768, 8, 1, None) == 1
+    assert lib.mxstream_mix(bufs, 0, bufs, 1, 32768, 8, 1, None) == 2
+    assert lib.mxstream_mix(bufs, 5, bufs, 1, 32768, 8, 1, None) == 2
+    assert lib.mxstream_mix(bufs, 3, bufs, 3, 32768, 8, 1, None) == 2
+    assert lib.mxstream_mix(bufs, 3, bufs, 2, 32768 + 16, 8, 1, None) == 2
+    assert lib.mxstream_mix(bufs, 3, bufs, 2, 32768, 6, 1, None) == 2
+    assert lib.mxstream_mix(bufs, 3, bufs, 2, 32768, 8, 0, None) == 2
+    odd = (ctypes.c_void_p * 2)(A + 8, A)
+    assert lib.mxstream_mix(odd, 2, bufs, 1, 32768, 8, 1, None) == 2

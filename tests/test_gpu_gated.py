@@ -3,7 +3,7 @@ SiLU as the control) through mxfp8_gated_fwd / mxfp8_gated_bwd.
 
 "Add swiglu + MXFP8 fused CuTe DSL kernel", API (the activation is a
 compile-time policy of one kernel source) and Follow-ups (more gated
-activations).  Same bar as the SwiGLU casts (tests/parity.py): codes within
+activations).  Same bar as the SwiGLU casts (oracle/parity.py): codes within
 one E4M3 step, scales bit-exact except next to a power-of-two boundary,
 invalid blocks exact.  The oracle evaluates each activation in double.
 """
@@ -14,7 +14,7 @@ import torch
 import swiglu_activation_cast_amd as mx
 from swiglu_activation_cast_amd import synth
 from helpers import all_bf16_bits, bits_to_torch_bf16, torch_bf16_to_bits
-from parity import compare_fused
+from oracle.parity import compare_fused
 
 pytestmark = pytest.mark.gpu
 
