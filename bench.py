@@ -424,6 +424,8 @@ def main():
 
 # read:write byte mix of each call (inputs : outputs per element): forward
 # 4 : 1.03 per layout, backward 6 : 2.06 per layout, the plain casts 2 : 1.03
+from swiglu_activation_cast_amd.metrics import STREAM_CONFIGS  # noqa: E402
+
 STREAM_MIXES = {"4:1": (4, 1), "2:1": (2, 1), "3:1": (3, 1), "3:2": (3, 2), "1:1": (1, 1)}
 CALL_MIX = {"fwd_row": "4:1", "fwd_col": "4:1", "fwd_both": "2:1", "bwd_row": "3:1", "bwd_col": "3:1",
             "bwd_both": "3:2", "quant2d_row": "2:1", "quant2d_col": "2:1", "quant3d_E64": "2:1",
@@ -447,13 +449,12 @@ def stream_ceilings(inp, bwd_out, stream):
     res = {}
     for name, (nr, nw) in STREAM_MIXES.items():
         best = None
-        for unroll in (4, 8):
-            for grid in (2048, 4096, 8192):
-                fn = lambda: stream_probe.mix(ins[:nr], outs[:nw], gib, unroll=unroll, grid=grid, stream=stream)
-                t, _ = time_launches(fn, 5, 2)
-                gbps = metrics.gbps((nr + nw) * gib, t)
-                if best is None or gbps > best[0]:
-                    best = (gbps, unroll, grid, t)
+        for unroll, grid in STREAM_CONFIGS:
+            fn = lambda: stream_probe.mix(ins[:nr], outs[:nw], gib, unroll=unroll, grid=grid, stream=stream)
+            t, _ = time_launches(fn, 5, 2)
+            gbps = metrics.gbps((nr + nw) * gib, t)
+            if best is None or gbps > best[0]:
+                best = (gbps, unroll, grid, t)
         res[name] = {"GB/s": round(best[0], 1), "frac": round(best[0] / metrics.HBM_PEAK_GBPS, 4),
                      "unroll": best[1], "grid": best[2], "us": round(best[3] * 1e6, 2)}
     print("bench: stream ceilings done", file=sys.stderr, flush=True)

@@ -26,7 +26,7 @@ extern "C" {
  *
  *   n_in  in 1..4, n_out in 1..2: the read:write byte mix is n_in : n_out.
  *   bytes a positive multiple of 4096 * unroll; every buffer 16-byte aligned.
- *   unroll 4 or 8: 16-byte accesses per buffer in flight in each thread.
+ *   unroll 2, 4 or 8: 16-byte accesses per buffer in flight in each thread.
  *   grid  workgroups (256 threads each), 1 .. 2^20; workgroup b handles
  *         chunks b, b + grid, ... of 4096 * unroll bytes of every buffer.
  *   stream a hipStream_t (NULL: the default stream).

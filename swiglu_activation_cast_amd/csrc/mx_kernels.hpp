@@ -225,36 +225,47 @@ constexpr size_t tiled_lds_bytes() {
   return (size_t)Op::OUT * kTC * kRS * sizeof(uint16_t);
 }
 
-#ifndef MX_MIN_WAVES
-#define MX_MIN_WAVES 1
-#endif
+// Waves per SIMD that the tile's LDS allows (160 KiB per CU, four waves per
+// workgroup, four SIMDs per CU): the register budget the kernel is held to,
+// so that registers never cut occupancy below what LDS permits.
+template <class Op>
+constexpr int tiled_waves() {
+  return (int)((160 * 1024) / tiled_lds_bytes<Op>());
+}
 
-template <class Op, bool ROWS>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVES, 8))) void k_tiled(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
-  const u32 L = xcd_remap(blockIdx.x, gridDim.x);
-  const int t = threadIdx.x;
+// Position of tile L (in launch order) of a tiled launch: batch e, first
+// row m0 and first source column n0.  Bands of a.band row tiles, row tiles
+// fastest inside a band.
+struct TilePos {
+  int64_t e, m0, n0;
+};
+
+__device__ __forceinline__ TilePos tile_pos(const Args &a, u32 L) {
   const u32 per = (u32)a.n_rt * (u32)a.n_ct;  // tiles per batch
-  const int64_t e = L / per;
   const u32 l = L % per;
-  // bands of a.band row tiles, row tiles fastest inside a band
   const u32 band_tiles = (u32)a.band * (u32)a.n_ct;
   const u32 band = l / band_tiles, in_band = l % band_tiles;
   const u32 rows_in_band = min((u32)a.band, (u32)a.n_rt - band * (u32)a.band);
   const u32 rt = band * (u32)a.band + in_band % rows_in_band, ct = in_band / rows_in_band;
-  const int64_t m0 = (int64_t)rt * kTM, n0 = (int64_t)ct * kTC;
+  return TilePos{(int64_t)(L / per), (int64_t)rt * kTM, (int64_t)ct * kTC};
+}
+
+template <class Op, bool ROWS>
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op>(), 8))) void k_tiled(const Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
+  const TilePos T = tile_pos(a, xcd_remap(blockIdx.x, gridDim.x));
+  const int t = threadIdx.x;
 
   // ---- load + compute: thread owns rows m0 + kRPT*rg + i, columns col..col+7
   const int cc = t % kCPR, rg = t / kCPR;
-  const int64_t col = n0 + cc * 8;
-  const bool colok = col < a.N;
+  const bool colok = T.n0 + cc * 8 < a.N;
   V4 out[kRPT][Op::OUT];
-  const int r0 = rg * kRPT;                  // first tile row of this thread
-  const u32 cl = colok ? (u32)cc * 8 : 0;    // lanes past N read column n0 (unused)
+  const int r0 = rg * kRPT;                // first tile row of this thread
+  const u32 cl = colok ? (u32)cc * 8 : 0;  // lanes past N read column n0 (unused)
   // Rows past M are read as row M-1 and columns past N as column n0: both
   // stay in bounds, and their values only reach 32-row blocks or a lane's
   // own columns that are never stored (M is a multiple of 32 here).
-  const u32 rmax = (u32)min<int64_t>(a.M - 1 - m0, kTM - 1);
+  const u32 rmax = (u32)min<int64_t>(a.M - 1 - T.m0, kTM - 1);
   {
     V4 in[kRPT][Op::IN];
 #pragma unroll
@@ -262,7 +273,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
       const u32 r = min((u32)(r0 + i), rmax);
 #pragma unroll
       for (int j = 0; j < Op::IN; j++) {
-        const uint16_t *tp = a.in[j] + e * a.bstride_in + m0 * a.ld_in[j] + n0;  // uniform
+        const uint16_t *tp = a.in[j] + T.e * a.bstride_in + T.m0 * a.ld_in[j] + T.n0;  // uniform
         in[i][j] = load16_stream(byte_off(tp, (r * (u32)a.ld_in[j] + cl) * 2u));
       }
     }
@@ -278,12 +289,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
         u32 am = max_xor2(max_xor1(amax_bits<4>(&out[i][o].x)));
         u32 b = e8m0_rceil(am);
         uint2 q = quant8(&out[i][o].x, b);
-        if (colok && m0 + r0 + i < a.M) {
-          const int64_t oc = o * a.N + n0;
-          uint8_t *qp = a.q_row + (m0 + i) * a.ld_q_row + oc;  // uniform
+        if (colok && T.m0 + r0 + i < a.M) {
+          const int64_t oc = o * a.N + T.n0;
+          uint8_t *qp = a.q_row + (T.m0 + i) * a.ld_q_row + oc;  // uniform
           store_stream(reinterpret_cast<unsigned long long *>(byte_off(qp, (u32)r0 * (u32)a.ld_q_row + cl)),
                        ((unsigned long long)q.y << 32) | q.x);
-          uint8_t *sp = a.s_row + (m0 + i) * a.ld_s_row + (oc >> 5);  // uniform
+          uint8_t *sp = a.s_row + (T.m0 + i) * a.ld_s_row + (oc >> 5);  // uniform
           if ((cc & 3) == 0) store_byte(byte_off(sp, (u32)r0 * (u32)a.ld_s_row + (cl >> 5)), (uint8_t)b);
         }
       }
@@ -291,53 +302,50 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(MX_MIN_WAVE
   }
 
   // ---- transpose into LDS: column (8*cc + k), rows kRPT*rg .. +kRPT-1, four at a time
-  auto to_lds = [&](int o, int slot) {
+#pragma unroll
+  for (int o = 0; o < Op::OUT; o++) {
 #pragma unroll
     for (int i0 = 0; i0 < kRPT; i0 += 4) {
 #pragma unroll
       for (int k = 0; k < 8; k++) {
-        const u32 *r0 = &out[i0][o].x, *r1 = &out[i0 + 1][o].x, *r2 = &out[i0 + 2][o].x, *r3 = &out[i0 + 3][o].x;
+        const u32 *w0 = &out[i0][o].x, *w1 = &out[i0 + 1][o].x, *w2 = &out[i0 + 2][o].x, *w3 = &out[i0 + 3][o].x;
         const int w = k >> 1;
         u32 p01, p23;
         if (k & 1) {
-          p01 = (r0[w] >> 16) | (r1[w] & 0xffff0000u);
-          p23 = (r2[w] >> 16) | (r3[w] & 0xffff0000u);
+          p01 = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
+          p23 = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
         } else {
-          p01 = (r0[w] & 0xffffu) | (r1[w] << 16);
-          p23 = (r2[w] & 0xffffu) | (r3[w] << 16);
+          p01 = (w0[w] & 0xffffu) | (w1[w] << 16);
+          p23 = (w2[w] & 0xffffu) | (w3[w] << 16);
         }
-        *reinterpret_cast<uint2 *>(&lds[slot][cc * 8 + k][rg * kRPT + i0]) = make_uint2(p01, p23);
+        *reinterpret_cast<uint2 *>(&lds[o][cc * 8 + k][rg * kRPT + i0]) = make_uint2(p01, p23);
       }
     }
-  };
+  }
+  __syncthreads();
 
   // ---- colwise: item = (column c, 16-row group g); lanes g, g^1 share a block
-  auto from_lds = [&](int o, int slot) {
+#pragma unroll
+  for (int o = 0; o < Op::OUT; o++) {
 #pragma unroll
     for (int p = 0; p < kTC * kG / kNT; p++) {
       const int i = t + kNT * p;
       const int g = i % kG, c = i / kG;
-      const V4 v0 = *reinterpret_cast<const V4 *>(&lds[slot][c][16 * g]);
-      const V4 v1 = *reinterpret_cast<const V4 *>(&lds[slot][c][16 * g + 8]);
+      const V4 v0 = *reinterpret_cast<const V4 *>(&lds[o][c][16 * g]);
+      const V4 v1 = *reinterpret_cast<const V4 *>(&lds[o][c][16 * g + 8]);
       const u32 v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       u32 am = max_xor1(amax_bits<8>(v));
       u32 b = e8m0_rceil(am);
       uint2 q0 = quant8(v, b), q1 = quant8(v + 4, b);
-      if (n0 + c < a.N && m0 + 16 * g < a.M) {
-        uint8_t *qp = a.q_col + e * a.bstride_q + (o * a.N + n0) * a.ld_q_col + m0;   // uniform
+      if (T.n0 + c < a.N && T.m0 + 16 * g < a.M) {
+        uint8_t *qp = a.q_col + T.e * a.bstride_q + (o * a.N + T.n0) * a.ld_q_col + T.m0;  // uniform
         store_stream(reinterpret_cast<u32x4_t *>(byte_off(qp, (u32)c * (u32)a.ld_q_col + 16 * g)),
                      u32x4_t{q0.x, q0.y, q1.x, q1.y});
-        uint8_t *sp = a.s_col + e * a.bstride_s + (o * a.N + n0) * a.ld_s_col + (m0 >> 5);  // uniform
+        uint8_t *sp = a.s_col + T.e * a.bstride_s + (o * a.N + T.n0) * a.ld_s_col + (T.m0 >> 5);  // uniform
         if ((g & 1) == 0) store_byte(byte_off(sp, (u32)c * (u32)a.ld_s_col + (g >> 1)), (uint8_t)b);
       }
     }
-  };
-
-#pragma unroll
-  for (int o = 0; o < Op::OUT; o++) to_lds(o, o);
-  __syncthreads();
-#pragma unroll
-  for (int o = 0; o < Op::OUT; o++) from_lds(o, o);
+  }
 }
 
 }  // namespace mx

@@ -61,7 +61,7 @@ const void *pick(int nr, int nw) {
 extern "C" int mxstream_mix(const void *const *in, int n_in, void *const *out, int n_out, int64_t bytes, int unroll,
                             int grid, void *stream) {
   if (!in || !out) return 1;
-  if (n_in < 1 || n_in > 4 || n_out < 1 || n_out > 2 || (unroll != 4 && unroll != 8)) return 2;
+  if (n_in < 1 || n_in > 4 || n_out < 1 || n_out > 2 || (unroll != 2 && unroll != 4 && unroll != 8)) return 2;
   if (grid < 1 || grid > (1 << 20) || bytes <= 0 || bytes % (4096 * (int64_t)unroll) != 0) return 2;
   StreamArgs a{};
   for (int j = 0; j < n_in; j++) {
@@ -75,7 +75,7 @@ extern "C" int mxstream_mix(const void *const *in, int n_in, void *const *out, i
     a.out[j] = static_cast<u32x4_t *>(out[j]);
   }
   a.n_chunks = bytes / (4096 * (int64_t)unroll);
-  const void *k = unroll == 4 ? pick<4>(n_in, n_out) : pick<8>(n_in, n_out);
+  const void *k = unroll == 2 ? pick<2>(n_in, n_out) : unroll == 4 ? pick<4>(n_in, n_out) : pick<8>(n_in, n_out);
   void *kargs[] = {&a};
   return hipLaunchKernel(k, dim3((unsigned)grid), dim3(256), kargs, 0, (hipStream_t)stream) == hipSuccess ? 0 : 7;
 }

@@ -12,6 +12,10 @@ from __future__ import annotations
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 matrix-core peak (no sparsity)
 
+# (16-byte accesses in flight per stream and thread, workgroups) of the
+# streaming-probe sweep that sets each read:write mix's ceiling
+STREAM_CONFIGS = ((2, 16384), (2, 32768), (4, 8192), (4, 16384), (4, 32768), (8, 16384))
+
 
 def _layouts(layout: int) -> int:
     return (layout & 1) + ((layout >> 1) & 1)

@@ -37,6 +37,7 @@ from . import _build, metrics, synth
 COPY_KERNEL = "k_stream<1, 1,"
 COPY_BYTES = 1 << 30  # the probe's buffers (bench.py stream_ceilings)
 THREADS = 256  # work-items per workgroup of every kernel the bench times
+STREAM_CONFIGS = metrics.STREAM_CONFIGS
 
 
 @dataclass
@@ -86,10 +87,8 @@ def bench_calls(workload: str, experts: int):
     ]
     gib = COPY_BYTES
     for mix, (nr, nw) in (("4:1", (4, 1)), ("2:1", (2, 1)), ("3:1", (3, 1)), ("3:2", (3, 2)), ("1:1", (1, 1))):
-        for u in (4, 8):
-            for grid in (2048, 4096, 8192):
-                calls.append(Call(f"k_stream<{nr}, {nw}, {u}>", f"stream_{mix}_u{u}_g{grid}", nr * gib, nw * gib,
-                                  grid))
+        for u, grid in STREAM_CONFIGS:
+            calls.append(Call(f"k_stream<{nr}, {nw}, {u}>", f"stream_{mix}_u{u}_g{grid}", nr * gib, nw * gib, grid))
     return calls
 
 
