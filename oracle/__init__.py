@@ -72,6 +72,11 @@ def _load():
         "orc_mx_gemm": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _p, _i64]),
         "orc_mx_grouped_gemm": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64,
                                                _i64, _p, _i64, _p, _i64]),
+        "orc_group_bounds": (ctypes.c_int, [_p, _i64, _i64, _p, _p]),
+        "orc_group_scale_base": (_i64, [_i64, _i64]),
+        "orc_pad_group_scales": (ctypes.c_int, [_p, _i64, _i64, _i64, _p, _i64, _p, _i64]),
+        "orc_mx_grouped_gemm_k": (ctypes.c_int, [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64,
+                                                 _p, _i64, _i64, _p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -334,4 +339,60 @@ def mx_grouped_gemm(a, sa, b, sb, offsets):
     _check(_load().orc_mx_grouped_gemm(_ptr(a), lda, _ptr(sa), ld_sa, _ptr(b), K, N * K, _ptr(sb), K // 32,
                                        N * (K // 32), _ptr(offs), G, M, N, K, _ptr(c), N, _ptr(cabs), N),
            "mx_grouped_gemm")
+    return c, cabs
+
+
+# ------------------------------------------------- token groups (wgrad)
+def _offs(offsets):
+    return np.ascontiguousarray(np.asarray(offsets, np.int32).reshape(-1))
+
+
+def group_bounds(offsets, T):
+    """(starts, ends) of the G token groups plus the tail group G, after
+    rounding each cumulative end down to a multiple of 32 and clamping the
+    ends to be non-decreasing and at most T.  int64 arrays of length G + 1."""
+    offs = _offs(offsets)
+    G = offs.size
+    st = np.zeros(G + 1, np.int64)
+    en = np.zeros(G + 1, np.int64)
+    _check(_load().orc_group_bounds(_ptr(offs), G, int(T), _ptr(st), _ptr(en)), "group_bounds")
+    return st, en
+
+
+def group_scale_base(g, start):
+    """Position of group g's first scale block in a per-group padded row."""
+    return int(_load().orc_group_scale_base(int(g), int(start)))
+
+
+def pad_group_scales(s, T, offsets, ld_out=None, fill=0):
+    """Per-group padded layout of colwise scales s [rows, T/32]; returns
+    [rows, ld_out] (default T/32 + 16 G) with unused positions = fill."""
+    s, ld_s = _u8_mat(s)
+    offs = _offs(offsets)
+    G = offs.size
+    rows = s.shape[0]
+    ld_out = T // 32 + 16 * G if ld_out is None else int(ld_out)
+    out = np.full((rows, ld_out), fill, np.uint8)
+    _check(_load().orc_pad_group_scales(_ptr(s), rows, ld_s, int(T), _ptr(offs), G, _ptr(out), ld_out),
+           "pad_group_scales")
+    return out
+
+
+def mx_grouped_gemm_k(a, sa, b, sb, offsets):
+    """K-grouped C_g = A_g B_g^T over each token group's columns of a [M, T]
+    and b [N, T] (E4M3 codes), scales sa [M, ld], sb [N, ld] in the per-group
+    padded layout.  Returns (C, sum |products|) as float64 [G, M, N]."""
+    a, lda = _u8_mat(a)
+    b, ldb = _u8_mat(b)
+    sa, ld_sa = _u8_mat(sa)
+    sb, ld_sb = _u8_mat(sb)
+    offs = _offs(offsets)
+    G = offs.size
+    M, T = a.shape
+    N = b.shape[0]
+    assert b.shape[1] == T and sa.shape[0] == M and sb.shape[0] == N
+    c = np.zeros((G, M, N), np.float64)
+    cabs = np.zeros((G, M, N), np.float64)
+    _check(_load().orc_mx_grouped_gemm_k(_ptr(a), lda, _ptr(sa), ld_sa, _ptr(b), ldb, _ptr(sb), ld_sb, _ptr(offs), G,
+                                         M, N, T, _ptr(c), N, M * N, _ptr(cabs)), "mx_grouped_gemm_k")
     return c, cabs

@@ -537,3 +537,101 @@ int orc_mx_grouped_gemm(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_
     }
     return 0;
 }
+
+/* ------------------------------------------------- token groups (wgrad) */
+
+/* Token groups along the blocked axis of a colwise cast ([P4, Perf
+ * analysis]: the weight-gradient GEMMs of a mixture-of-experts layer
+ * contract over each expert's tokens; [P4, Summary and review comments]:
+ * per-group scale buffers are sized by an upper bound on their padding).
+ * offs[0..G-1] are cumulative group ends.  Each end is rounded down to a
+ * multiple of 32 (a scale block never straddles two groups), negative ends
+ * count as 0, and the ends are made non-decreasing and at most T:
+ *   end_g = min(max(round32(offs[g]), end_{g-1}), T),  end_{-1} = 0.
+ * Group g is tokens [end_{g-1}, end_g); tokens from end_{G-1} to T form a
+ * tail group G.  starts/ends receive G + 1 entries (the tail included). */
+int orc_group_bounds(const int32_t *offs, int64_t G, int64_t T, int64_t *starts, int64_t *ends)
+{
+    if (G < 0 || T < 0)
+        return -1;
+    int64_t prev = 0;
+    for (int64_t g = 0; g <= G; g++) {
+        int64_t e;
+        if (g == G) {
+            e = T;
+        } else {
+            e = offs[g] <= 0 ? 0 : ((int64_t)offs[g] / 32) * 32;
+            if (e < prev)
+                e = prev;
+            if (e > T)
+                e = T;
+        }
+        starts[g] = prev;
+        ends[g] = e;
+        prev = e;
+    }
+    return 0;
+}
+
+/* Position, in a per-group padded scale row, of the first block of the group
+ * that starts at token s: 16 * (g + floor(s / 512)).  It is a multiple of 16
+ * (every group's scales start 16-byte aligned), group g + 1's region starts
+ * after group g's last block, and no position reaches T/32 + 16 G. */
+int64_t orc_group_scale_base(int64_t g, int64_t s)
+{
+    return 16 * (g + s / 512);
+}
+
+/* Per-group padded layout of colwise scales: the plain scale matrix s
+ * [rows, T/32] (row stride ld_s) rewritten so that the blocks of each group
+ * (the tail group included) start at orc_group_scale_base in every row of
+ * out (row stride ld_out >= T/32 + 16 G).  Positions no block maps to are
+ * left as they are.  T must be a multiple of 32. */
+int orc_pad_group_scales(const uint8_t *s, int64_t rows, int64_t ld_s, int64_t T, const int32_t *offs, int64_t G,
+                         uint8_t *out, int64_t ld_out)
+{
+    if (rows < 0 || T < 0 || T % 32 != 0 || G < 0 || ld_out < T / 32 + 16 * G)
+        return -1;
+    int64_t *st = (int64_t *)malloc(sizeof(int64_t) * 2 * (size_t)(G + 1));
+    if (!st)
+        return -2;
+    int64_t *en = st + G + 1;
+    orc_group_bounds(offs, G, T, st, en);
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t g = 0; g <= G; g++) {
+            int64_t base = orc_group_scale_base(g, st[g]);
+            for (int64_t b = st[g] / 32; b < en[g] / 32; b++)
+                out[r * ld_out + base + (b - st[g] / 32)] = s[r * ld_s + b];
+        }
+    free(st);
+    return 0;
+}
+
+/* K-grouped form of the consumer (the weight gradient): the contraction
+ * axis (tokens, T of them) is split into the groups above, and group g's
+ * result is the plain C_g = A_g B_g^T over its own tokens, where A_g is
+ * columns [start_g, end_g) of a [M, T] (and B_g of b [N, T]), with scales
+ * read from the per-group padded layout (group g's first block at
+ * orc_group_scale_base).  c holds G results [M, N], c + g * stride_c.  An
+ * empty group gives zeros.  T must be a multiple of 32. */
+int orc_mx_grouped_gemm_k(const uint8_t *a, int64_t lda, const uint8_t *sa, int64_t ld_sa,
+                          const uint8_t *b, int64_t ldb, const uint8_t *sb, int64_t ld_sb,
+                          const int32_t *offs, int64_t G, int64_t M, int64_t N, int64_t T,
+                          double *c, int64_t ldc, int64_t stride_c, double *cabs)
+{
+    if (G < 0 || M < 0 || N < 0 || T < 0 || T % 32 != 0)
+        return -1;
+    int64_t *st = (int64_t *)malloc(sizeof(int64_t) * 2 * (size_t)(G + 1));
+    if (!st)
+        return -2;
+    int64_t *en = st + G + 1;
+    orc_group_bounds(offs, G, T, st, en);
+    int rc = 0;
+    for (int64_t g = 0; g < G && rc == 0; g++) {
+        int64_t base = orc_group_scale_base(g, st[g]);
+        rc = orc_mx_gemm(a + st[g], lda, sa + base, ld_sa, b + st[g], ldb, sb + base, ld_sb, M, N,
+                         en[g] - st[g], c + g * stride_c, ldc, cabs ? cabs + g * stride_c : NULL, ldc);
+    }
+    free(st);
+    return rc;
+}
