@@ -238,6 +238,74 @@ mxfp8_status mxfp8_grouped_gemm(const void *a, int64_t lda, const void *sa, int6
                                 const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K,
                                 float *c, int64_t ldc, void *stream);
 
+/*
+ * Token groups and the per-group padded colwise scale layout (the weight-
+ * gradient side of a mixture-of-experts step).  "[mxfp8 moe training] add
+ * compile support", Perf analysis (the colwise casts feed grouped GEMMs
+ * that contract over each expert's tokens) and Summary with its review
+ * comments (per-group scale buffers sized by an upper bound on their
+ * padding, with the offsets left on the device).
+ *
+ * The M rows (tokens) of a cast are split into groups by group_ends, a
+ * DEVICE int32 array of n_groups cumulative ends, read on the GPU only.  Each
+ * end is rounded down to a multiple of 32 (a scale block never straddles two
+ * groups; real group sizes should be multiples of 32), negative ends count
+ * as 0, and the ends are made non-decreasing and at most M:
+ *   end_g = min(max(round32(group_ends[g]), end_{g-1}), M),  end_{-1} = 0.
+ * Group g is rows [end_{g-1}, end_g); rows from end_{n-1} to M form a tail
+ * group n.  In every colwise scale row, the scale of the 32-row block that
+ * starts at row t of group g (which starts at row s) is stored at position
+ *   16 * (g + floor(s / 512)) + (t - s) / 32,
+ * so every group's scales start 16-byte aligned, groups never overlap, and
+ * every position is below M/32 + 16 * n_groups: ld_s_col must be at least
+ * that.  Positions no block maps to are not written.  With one group
+ * ending at M the layout is the plain one.  Any group_ends values give
+ * in-range positions.
+ *
+ * The grouped casts are the casts above with that colwise scale layout;
+ * everything else (codes, rowwise outputs, checks) is unchanged.  Extra
+ * checks: 1 <= n_groups <= 1024 (else MXFP8_ERR_SHAPE), group_ends non-NULL
+ * (MXFP8_ERR_NULL) and 4-byte aligned (MXFP8_ERR_ALIGN), M < 2^31 - 256
+ * (MXFP8_ERR_OVERFLOW).
+ */
+mxfp8_status mxfp8_gated_fwd_grouped(int act, const void *gate, int64_t ld_gate,
+                                     const void *up, int64_t ld_up, int64_t M, int64_t N, int layout,
+                                     void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                                     void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                                     const int32_t *group_ends, int64_t n_groups, void *stream);
+mxfp8_status mxfp8_gated_bwd_grouped(int act, const void *dh, int64_t ld_dh,
+                                     const void *gate, int64_t ld_gate, const void *up, int64_t ld_up,
+                                     int64_t M, int64_t N, int layout,
+                                     void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                                     void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                                     const int32_t *group_ends, int64_t n_groups, void *stream);
+mxfp8_status mxfp8_quant_2d_grouped(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout,
+                                    void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                                    void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                                    const int32_t *group_ends, int64_t n_groups, void *stream);
+
+/*
+ * K-grouped form of mxfp8_gemm: the weight gradient, which contracts over
+ * each group's tokens ("[mxfp8 moe training] add compile support", Perf
+ * analysis).  a [M, T] and b [N, T] hold E4M3 codes with the T tokens along
+ * the rows (the colwise outputs of two [T, *] matrices); their scales sa
+ * [M, ld_sa] and sb [N, ld_sb] are in the per-group padded layout above
+ * (the grouped casts' colwise scales), for the same group_ends.  For each of
+ * the G groups (bounds as above, with T in place of M; the tail group is
+ * not used):
+ *   C_g = A[:, start_g:end_g] B[:, start_g:end_g]^T,  fp32 [M, N],
+ * written at c + g * stride_c (row stride ldc).  An empty group gives zeros.
+ *   Requires T % 32 == 0, lda, ldb >= T and multiples of 16, ld_sa, ld_sb >=
+ *   T/32 + 16 G, stride_c >= (M-1)*ldc + N, 1 <= G <= 1024 (G == 0 returns
+ *   MXFP8_OK and launches nothing).  group_ends is read on the GPU only.
+ * Same numerics as mxfp8_gemm; with every ld_sa, ld_sb a multiple of 16 the
+ * scales of every group are fetched 16 bytes at a time.
+ */
+mxfp8_status mxfp8_grouped_gemm_k(const void *a, int64_t lda, const void *sa, int64_t ld_sa,
+                                  const void *b, int64_t ldb, const void *sb, int64_t ld_sb,
+                                  const int32_t *group_ends, int64_t G, int64_t M, int64_t N, int64_t T,
+                                  float *c, int64_t ldc, int64_t stride_c, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char *mxfp8_status_str(mxfp8_status status);
 

@@ -50,6 +50,11 @@ _SIGNATURES = {
     "mxfp8_grouped_gemm": [_p, _i64, _p, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64,
                            _p],
     "mxfp8_swiglu_bwd_bf16": [_p, _i64, _p, _i64, _p, _i64, _i64, _i64, _p, _i64, _p],
+    "mxfp8_gated_fwd_grouped": [_int, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p, _i64, _p],
+    "mxfp8_gated_bwd_grouped": [_int, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _int] + [_p, _i64] * 4
+                               + [_p, _i64, _p],
+    "mxfp8_quant_2d_grouped": [_p, _i64, _i64, _i64, _int] + [_p, _i64] * 4 + [_p, _i64, _p],
+    "mxfp8_grouped_gemm_k": [_p, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _i64, _i64, _p, _i64, _i64, _p],
 }
 
 _lib = None
@@ -116,22 +121,29 @@ def _layout(rowwise: bool, colwise: bool) -> int:
     return layout
 
 
-def alloc_outputs(M: int, W: int, layout: int, device) -> Tuple[torch.Tensor, ...]:
-    """Empty (q_row, q_col, s_row, s_col) for an [M, W] result."""
+def alloc_outputs(M: int, W: int, layout: int, device, n_groups: int = 0) -> Tuple[torch.Tensor, ...]:
+    """Empty (q_row, q_col, s_row, s_col) for an [M, W] result.  With token
+    groups (n_groups > 0) s_col is [W, M/32 + 16 n_groups], the per-group
+    padded layout (positions no block maps to are zero)."""
     empty = torch.empty(0, dtype=torch.uint8, device=device)
     q_row = torch.empty((M, W), dtype=torch.uint8, device=device) if layout & ROWWISE else empty
     s_row = torch.empty((M, W // 32), dtype=torch.uint8, device=device) if layout & ROWWISE else empty
     q_col = torch.empty((W, M), dtype=torch.uint8, device=device) if layout & COLWISE else empty
-    s_col = torch.empty((W, M // 32), dtype=torch.uint8, device=device) if layout & COLWISE else empty
+    if layout & COLWISE:
+        s_col = (torch.zeros if n_groups else torch.empty)((W, M // 32 + 16 * n_groups), dtype=torch.uint8,
+                                                             device=device)
+    else:
+        s_col = empty
     return q_row, q_col, s_row, s_col
 
 
-def _out_args(outs: Sequence[torch.Tensor], layout: int, M: int, W: int, device):
+def _out_args(outs: Sequence[torch.Tensor], layout: int, M: int, W: int, device, n_groups: int = 0):
     """(pointer, leading dimension) pairs of the four outputs of an [M, W]
     result.  The C ABI cannot see buffer sizes, so every enabled output is
     checked here against its full extent: q_row [M, W], s_row [M, W/32],
-    q_col [W, M], s_col [W, M/32], uint8, on the inputs' device, unit column
-    stride (a larger row stride is allowed)."""
+    q_col [W, M], s_col [W, M/32] (with token groups [W, M/32 + 16
+    n_groups], the per-group padded layout), uint8, on the inputs' device,
+    unit column stride (a larger row stride is allowed)."""
     if len(outs) != 4:
         raise ValueError("out must be (q_row, q_col, s_row, s_col)")
     q_row, q_col, s_row, s_col = outs
@@ -152,7 +164,7 @@ def _out_args(outs: Sequence[torch.Tensor], layout: int, M: int, W: int, device)
 
     rows, cols = layout & ROWWISE, layout & COLWISE
     return (mat(q_row, rows, "q_row", M, W) + mat(s_row, rows, "s_row", M, W // 32)
-            + mat(q_col, cols, "q_col", W, M) + mat(s_col, cols, "s_col", W, M // 32))
+            + mat(q_col, cols, "q_col", W, M) + mat(s_col, cols, "s_col", W, M // 32 + 16 * n_groups))
 
 
 def mxfp8_swiglu_fwd(gate: torch.Tensor, up: torch.Tensor, *, rowwise: bool = True, colwise: bool = False,
@@ -386,4 +398,102 @@ def mxfp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: t
     st = lib().mxfp8_grouped_gemm(pa, lda, psa, ld_sa, b.data_ptr(), ldb, stride_b, sb.data_ptr(), ld_sb, stride_sb,
                                   offsets.data_ptr(), G, M, N, K, out.data_ptr(), ldc, _stream(a.device, stream))
     _check("mxfp8_grouped_gemm", st)
+    return out
+
+
+# ------------------------------------------------------------ token groups
+def _group_ends(group_ends: torch.Tensor, device) -> Tuple[int, int]:
+    if group_ends.dtype != torch.int32 or group_ends.dim() != 1 or group_ends.device != torch.device(device):
+        raise ValueError("group_ends must be a 1-D int32 tensor on the inputs' device")
+    if group_ends.shape[0] > 1 and group_ends.stride(0) != 1:
+        raise ValueError("group_ends must be contiguous")
+    return group_ends.data_ptr(), group_ends.shape[0]
+
+
+def mxfp8_gated_fwd_grouped(gate: torch.Tensor, up: torch.Tensor, group_ends: torch.Tensor, *, act="silu",
+                            rowwise: bool = True, colwise: bool = True, out: Optional[Sequence[torch.Tensor]] = None,
+                            stream=None):
+    """mxfp8_gated_fwd with token groups: colwise scales in the per-group
+    padded layout [N, M/32 + 16 G] (group_ends: device int32 [G], cumulative
+    row ends); returns (q_row, q_col, s_row, s_col)."""
+    code = _act_code(act)
+    layout = _layout(rowwise, colwise)
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if gate.shape != up.shape or gate.device != up.device:
+        raise ValueError("gate and up must have the same shape and device")
+    M, N = gate.shape
+    pe, G = _group_ends(group_ends, gate.device)
+    outs = out if out is not None else alloc_outputs(M, N, layout, gate.device, G)
+    st = lib().mxfp8_gated_fwd_grouped(code, pg, ldg, pu, ldu, M, N, layout,
+                                       *_out_args(outs, layout, M, N, gate.device, G), pe, G,
+                                       _stream(gate.device, stream))
+    _check("mxfp8_gated_fwd_grouped", st)
+    return tuple(outs)
+
+
+def mxfp8_gated_bwd_grouped(dh: torch.Tensor, gate: torch.Tensor, up: torch.Tensor, group_ends: torch.Tensor, *,
+                            act="silu", rowwise: bool = True, colwise: bool = True,
+                            out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """mxfp8_gated_bwd with token groups: colwise scales of [dgate | dup] in
+    the per-group padded layout [2N, M/32 + 16 G]."""
+    code = _act_code(act)
+    layout = _layout(rowwise, colwise)
+    pd, ldd = _bf16_matrix(dh, "dh")
+    pg, ldg = _bf16_matrix(gate, "gate")
+    pu, ldu = _bf16_matrix(up, "up")
+    if not (dh.shape == gate.shape == up.shape) or not (dh.device == gate.device == up.device):
+        raise ValueError("dh, gate and up must have the same shape and device")
+    M, N = gate.shape
+    pe, G = _group_ends(group_ends, gate.device)
+    outs = out if out is not None else alloc_outputs(M, 2 * N, layout, gate.device, G)
+    st = lib().mxfp8_gated_bwd_grouped(code, pd, ldd, pg, ldg, pu, ldu, M, N, layout,
+                                       *_out_args(outs, layout, M, 2 * N, gate.device, G), pe, G,
+                                       _stream(gate.device, stream))
+    _check("mxfp8_gated_bwd_grouped", st)
+    return tuple(outs)
+
+
+def mxfp8_quant_2d_grouped(x: torch.Tensor, group_ends: torch.Tensor, *, rowwise: bool = False, colwise: bool = True,
+                           out: Optional[Sequence[torch.Tensor]] = None, stream=None):
+    """mxfp8_quant_2d with token groups along M: colwise scales in the
+    per-group padded layout [K, M/32 + 16 G]."""
+    layout = _layout(rowwise, colwise)
+    px, ldx = _bf16_matrix(x, "x")
+    M, K = x.shape
+    pe, G = _group_ends(group_ends, x.device)
+    outs = out if out is not None else alloc_outputs(M, K, layout, x.device, G)
+    st = lib().mxfp8_quant_2d_grouped(px, ldx, M, K, layout, *_out_args(outs, layout, M, K, x.device, G), pe, G,
+                                      _stream(x.device, stream))
+    _check("mxfp8_quant_2d_grouped", st)
+    return tuple(outs)
+
+
+def mxfp8_grouped_gemm_k(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                         group_ends: torch.Tensor, *, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """K-grouped C_g = A_g B_g^T (fp32 [G, M, N]): a [M, T] and b [N, T]
+    E4M3 codes (the colwise outputs of [T, M] and [T, N] matrices), scales
+    sa [M, >= T/32 + 16 G] and sb [N, ...] in the per-group padded layout of
+    group_ends (device int32 [G])."""
+    pa, lda = _u8_matrix(a, "a")
+    pb, ldb = _u8_matrix(b, "b")
+    psa, ld_sa = _u8_matrix(sa, "sa")
+    psb, ld_sb = _u8_matrix(sb, "sb")
+    M, T = a.shape
+    N = b.shape[0]
+    pe, G = _group_ends(group_ends, a.device)
+    if b.shape[1] != T or sa.shape[0] != M or sb.shape[0] != N:
+        raise ValueError("shapes must be a [M, T], b [N, T], sa [M, *], sb [N, *]")
+    if sa.shape[1] < T // 32 + 16 * G or sb.shape[1] < T // 32 + 16 * G:
+        raise ValueError(f"padded scale rows need at least T/32 + 16 G = {T // 32 + 16 * G} columns")
+    if out is None:
+        out = torch.empty((G, M, N), dtype=torch.float32, device=a.device)
+    elif (out.dtype != torch.float32 or tuple(out.shape) != (G, M, N) or (N > 1 and out.stride(2) != 1)
+          or out.device != a.device):
+        raise ValueError(f"out must be a float32 [{G}, {M}, {N}] tensor with unit column stride")
+    ldc = out.stride(1) if M > 1 else max(N, 1)
+    stride_c = out.stride(0) if G > 1 else max(ldc * M, 1)
+    st = lib().mxfp8_grouped_gemm_k(pa, lda, psa, ld_sa, pb, ldb, psb, ld_sb, pe, G, M, N, T, out.data_ptr(), ldc,
+                                    stride_c, _stream(a.device, stream))
+    _check("mxfp8_grouped_gemm_k", st)
     return out

@@ -46,7 +46,15 @@ struct GemmArgs {
   // scale rows start 16-byte aligned (sa, sb, ld_sa, ld_sb, stride_sb all
   // multiples of 16): the scale table is then fetched 16 bytes at a time
   int32_t scale_vec;
+  // K-grouped form: group g's result at c + g * stride_c
+  int64_t stride_c;
 };
+
+// Kernel forms: the plain GEMM; rows of A grouped by device-side offsets
+// (each group against its own expert's B: forward and input gradient); and
+// the contraction axis grouped (each group of tokens gives its own C: the
+// weight gradient).
+enum GemmMode { kGemmPlain = 0, kGemmGroupM = 1, kGemmGroupK = 2 };
 
 constexpr int kMaxGroups = 1024;
 
@@ -75,7 +83,7 @@ __device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
 // different 4-bank groups.
 __device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 1) & 7u)) << 4); }
 
-template <bool GROUPED>
+template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t smemA[2][kStageA], smemB[2][kStageB];  // [buffer]
   // scale table of one group of kSG blocks: row q < kBM is A's tile row q,
@@ -85,8 +93,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
 
   // Tile order: each XCD takes one contiguous range of tiles; inside it,
-  // groups of kGroup tile rows are walked column by column.
-  const u32 L = xcd_remap(blockIdx.x, gridDim.x);
+  // groups of kGroup tile rows are walked column by column.  In the
+  // K-grouped form the tiles of one token group come one after another.
+  u32 L = xcd_remap(blockIdx.x, gridDim.x);
+  int64_t kgrp = 0;
+  if constexpr (MODE == kGemmGroupK) {
+    const u32 per = (u32)g.tiles_m * (u32)g.tiles_n;
+    kgrp = L / per;
+    L %= per;
+  }
   const u32 per_group = (u32)kGroup * (u32)g.tiles_n;
   const u32 grp = L / per_group, in_grp = L % per_group;
   const u32 rows_in_grp = min((u32)kGroup, (u32)g.tiles_m - grp * (u32)kGroup);
@@ -99,7 +114,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   // tiles (rows / 256 + groups), and tiles past the real count do nothing.
   int64_t m_base = tm * kBM, m_end = g.M;
   const uint8_t *b_mat = g.b, *sb_mat = g.sb;
-  if constexpr (GROUPED) {
+  // Contraction range [k_lo, k_lo + Kt) of the operands' columns, and the
+  // column of its first scale block.
+  int64_t k_lo = 0, Kt = g.K, s_lo = 0;
+  float *c_mat = g.c;
+  if constexpr (MODE == kGemmGroupM) {
     __shared__ int32_t offs_s[kMaxGroups];
     for (int e = t; e < g.G; e += kGemmThreads) offs_s[e] = g.offs[e];
     __syncthreads();
@@ -121,18 +140,35 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     b_mat = g.b + (int64_t)e_hit * g.stride_b;
     sb_mat = g.sb + (int64_t)e_hit * g.stride_sb;
   }
+  if constexpr (MODE == kGemmGroupK) {
+    // Token group kgrp: the cumulative ends rounded down to a multiple of 32
+    // (negative ends read as 0), made non-decreasing and at most K; its
+    // scales start at 16 (kgrp + floor(start / 512)) of each scale row (the
+    // per-group padded layout the grouped casts write).
+    int64_t start = 0, end = 0;
+    for (int64_t e = 0; e <= kgrp; e++) {  // uniform
+      const int32_t v = g.offs[e];
+      const int64_t r = v <= 0 ? 0 : (int64_t)(v & ~31);
+      start = end;
+      end = min<int64_t>(max<int64_t>(r, start), g.K);
+    }
+    k_lo = start;
+    Kt = end - start;
+    s_lo = 16 * (kgrp + start / 512);
+    c_mat = g.c + kgrp * g.stride_c;
+  }
 
   // Rows past M (N) are read as the last row: in bounds, never stored.
-  const uint8_t *a_tile = g.a + m_base * g.lda, *b_tile = b_mat + n_base * g.ldb;  // uniform
+  const uint8_t *a_tile = g.a + m_base * g.lda + k_lo, *b_tile = b_mat + n_base * g.ldb + k_lo;  // uniform
   const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
 
   // ---- scales: moved to LDS kSG blocks (kStagesPerGroup stages) at a
   // time, thread t taking A's and B's tile row t.  Blocks past K / 32 read
   // as 127 (2^0) against zero data.  One byte load per lane per operand
   // tile and stage, from 32 rows at once, is far slower than this.
-  const uint8_t *sa_tile = g.sa + m_base * g.ld_sa, *sb_tile = sb_mat + n_base * g.ld_sb;  // uniform
-  const int64_t nblk = g.K / 32;
-  const int nstage = (int)((g.K + kBK - 1) / kBK);
+  const uint8_t *sa_tile = g.sa + m_base * g.ld_sa + s_lo, *sb_tile = sb_mat + n_base * g.ld_sb + s_lo;  // uniform
+  const int64_t nblk = Kt / 32;
+  const int nstage = (int)((Kt + kBK - 1) / kBK);
   const int ngroup = (int)((nblk + kSG - 1) / kSG);
   const u32 sa_row = min((u32)t, a_rows - 1), sb_row = min((u32)t, b_rows - 1);
 
@@ -192,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     for (int q = 0; q < 8; q++) {
       const u32 p = (u32)w * 8u + (u32)q;
       const u32 row = 8u * p + ((u32)lane >> 3), kc = ((u32)lane & 7u) ^ ((row >> 1) & 7u);
-      const bool in_k = k0 + 16 * (int64_t)kc < g.K;
+      const bool in_k = k0 + 16 * (int64_t)kc < Kt;
       const u32 ra = min(row, a_rows - 1), rb = min(row, b_rows - 1);
       const uint8_t *pa = in_k ? byte_off(a_tile + k0, ra * (u32)g.lda + kc * 16u) : kZeroChunk;
       const uint8_t *pb = in_k ? byte_off(b_tile + k0, rb * (u32)g.ldb + kc * 16u) : kZeroChunk;
@@ -284,7 +320,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
-        if (row < m_end && col < g.N) *gptr(g.c + row * g.ldc + col) = acc[i][j][v];
+        if (row < m_end && col < g.N) *gptr(c_mat + row * g.ldc + col) = acc[i][j][v];
       }
     }
 }

@@ -49,6 +49,11 @@ struct Args {
   int64_t bstride_in, bstride_q, bstride_s;  // per-batch offsets (3D cast)
   int32_t n_rt, n_ct;                        // row tiles, column tiles
   int32_t band;                              // row tiles per band (tile order)
+  // Token groups of the colwise scales (n_grp > 0): cumulative group ends
+  // in device memory; colwise scales are then written in the per-group
+  // padded layout (group_block_pos).
+  const int32_t *grp;
+  int32_t n_grp;
 };
 
 __device__ __forceinline__ V4 load16(const uint16_t *p) { return *reinterpret_cast<const V4 *>(p); }
@@ -250,11 +255,61 @@ __device__ __forceinline__ TilePos tile_pos(const Args &a, u32 L) {
   return TilePos{(int64_t)(L / per), (int64_t)rt * kTM, (int64_t)ct * kTC};
 }
 
-template <class Op, bool ROWS>
+// Per-group padded colwise scale positions ("[mxfp8 moe training] add
+// compile support", Summary and review comments: per-group scale buffers
+// sized by an upper bound on their padding).  Tokens (rows of the cast) are
+// split into groups by the cumulative ends grp[0..n-1], each rounded down to
+// a multiple of 32, negative ends read as 0, and the ends made
+// non-decreasing and at most M; the tokens after the last end form a tail
+// group n.  The scale of the block that starts at token t, in group g that
+// starts at token s, sits at 16 (g + floor(s / 512)) + (t - s) / 32 of its
+// scale row: every group's run starts 16-byte aligned, runs never overlap,
+// and no position reaches M/32 + 16 n.
+//
+// For a row of blocks starting at tokens t_k = m0 + 32 k (k = 0..3, t_k < M)
+// the wavefront finds g = the first index whose rounded end exceeds t (the
+// ends before it are all <= t, so the clamped end of group g - 1 is their
+// maximum, which is s).  Lanes read 64 ends at a time; a ballot finds the
+// first end past t and a max reduction over the lanes before it gives s.
+__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d));
+  return v;
+}
+
+__device__ __forceinline__ void group_block_pos(const int32_t *grp, int32_t n, int64_t m0, u32 pos[4]) {
+  const int lane = threadIdx.x & 63;
+  int32_t g[4] = {-1, -1, -1, -1}, s[4] = {0, 0, 0, 0};
+  for (int32_t j0 = 0; j0 < n; j0 += 64) {  // uniform
+    const int32_t j = j0 + lane;
+    const int32_t ej = *gptr(grp + min(j, n - 1));  // in bounds for every lane
+    const int32_t e = j < n ? ej : INT32_MAX;
+    const int32_t r = e <= 0 ? 0 : (e & ~31);  // ends past the list read as "past every token"
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      if (g[k] >= 0) continue;  // uniform
+      const int32_t t = (int32_t)m0 + 32 * k;
+      const unsigned long long past = __ballot(r > t);
+      const int first = past ? __builtin_ctzll(past) : 64;
+      s[k] = max(s[k], wave_max_i32(lane < first ? r : 0));
+      if (past) g[k] = j0 + first;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int32_t gk = g[k] < 0 ? n : g[k];
+    const int32_t t = (int32_t)m0 + 32 * k;
+    pos[k] = (u32)(16 * (gk + s[k] / 512) + (t - s[k]) / 32);
+  }
+}
+
+template <class Op, bool ROWS, bool GROUPS = false>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op>(), 8))) void k_tiled(const Args a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
   const TilePos T = tile_pos(a, xcd_remap(blockIdx.x, gridDim.x));
   const int t = threadIdx.x;
+  u32 gpos[4] = {0, 0, 0, 0};  // padded positions of the tile's four row blocks (token groups)
+  if constexpr (GROUPS) group_block_pos(a.grp, a.n_grp, T.m0, gpos);
 
   // ---- load + compute: thread owns rows m0 + kRPT*rg + i, columns col..col+7
   const int cc = t % kCPR, rg = t / kCPR;
@@ -341,8 +396,11 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
         uint8_t *qp = a.q_col + T.e * a.bstride_q + (o * a.N + T.n0) * a.ld_q_col + T.m0;  // uniform
         store_stream(reinterpret_cast<u32x4_t *>(byte_off(qp, (u32)c * (u32)a.ld_q_col + 16 * g)),
                      u32x4_t{q0.x, q0.y, q1.x, q1.y});
-        uint8_t *sp = a.s_col + T.e * a.bstride_s + (o * a.N + T.n0) * a.ld_s_col + (T.m0 >> 5);  // uniform
-        if ((g & 1) == 0) store_byte(byte_off(sp, (u32)c * (u32)a.ld_s_col + (g >> 1)), (uint8_t)b);
+        uint8_t *sp = a.s_col + T.e * a.bstride_s + (o * a.N + T.n0) * a.ld_s_col;  // uniform
+        const int k = g >> 1;
+        const u32 sb = GROUPS ? (k == 0 ? gpos[0] : k == 1 ? gpos[1] : k == 2 ? gpos[2] : gpos[3])
+                              : (u32)(T.m0 >> 5) + (u32)k;
+        if ((g & 1) == 0) store_byte(byte_off(sp, (u32)c * (u32)a.ld_s_col + sb), (uint8_t)b);
       }
     }
   }

@@ -73,7 +73,7 @@ bool tile_offsets_ok(const int64_t *ld_in, int n_in, int64_t ld_q_row, int64_t l
 mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, int n_in, int64_t M,
                       int64_t N, int layout, const void *q_row, int64_t ld_q_row, const void *s_row,
                       int64_t ld_s_row, const void *q_col, int64_t ld_q_col, const void *s_col,
-                      int64_t ld_s_col) {
+                      int64_t ld_s_col, int64_t n_groups = 0) {
   if (layout < MXFP8_ROWWISE || layout > MXFP8_BOTH) return MXFP8_ERR_LAYOUT;
   if (M < 0 || N < 0) return MXFP8_ERR_SHAPE;
   const bool rows = layout & MXFP8_ROWWISE, cols = layout & MXFP8_COLWISE;
@@ -90,7 +90,10 @@ mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, in
   for (int j = 0; j < n_in; j++)
     if (ld_in[j] < N || ld_in[j] % 8 != 0) return MXFP8_ERR_STRIDE;
   if (rows && (ld_q_row < W || ld_q_row % 16 != 0 || ld_s_row < W / 32)) return MXFP8_ERR_STRIDE;
-  if (cols && (ld_q_col < M || ld_q_col % 16 != 0 || ld_s_col < M / 32)) return MXFP8_ERR_STRIDE;
+  // colwise scale rows: M/32 blocks, or with token groups the per-group
+  // padded layout, whose positions stay below M/32 + 16 groups
+  const int64_t s_col_w = M / 32 + 16 * n_groups;
+  if (cols && (ld_q_col < M || ld_q_col % 16 != 0 || ld_s_col < s_col_w)) return MXFP8_ERR_STRIDE;
   for (int j = 0; j < n_in; j++)
     if (!aligned16(in[j])) return MXFP8_ERR_ALIGN;
   if (rows && !aligned16(q_row)) return MXFP8_ERR_ALIGN;
@@ -98,7 +101,7 @@ mxfp8_status check_2d(Kind kind, const void *const *in, const int64_t *ld_in, in
   for (int j = 0; j < n_in; j++)
     if (!extent_ok(M, N, ld_in[j])) return MXFP8_ERR_OVERFLOW;
   if (rows && (!extent_ok(M, W, ld_q_row) || !extent_ok(M, W / 32, ld_s_row))) return MXFP8_ERR_OVERFLOW;
-  if (cols && (!extent_ok(W, M, ld_q_col) || !extent_ok(W, M / 32, ld_s_col))) return MXFP8_ERR_OVERFLOW;
+  if (cols && (!extent_ok(W, M, ld_q_col) || !extent_ok(W, s_col_w, ld_s_col))) return MXFP8_ERR_OVERFLOW;
   if (cols && !tile_offsets_ok(ld_in, n_in, rows ? ld_q_row : 0, rows ? ld_s_row : 0, ld_q_col, ld_s_col))
     return MXFP8_ERR_OVERFLOW;
   return MXFP8_OK;
@@ -135,7 +138,7 @@ unsigned lds_pad_for_cap(int cap, size_t static_lds) {
 // Launch of the colwise / both-layout kernel over `batches` stacked [M, N]
 // problems (batches > 1 only for the 3D cast); `cap` is the workgroups per
 // CU for a colwise-only launch (0: as many as fit).
-template <class Op>
+template <class Op, bool GROUPS = false>
 mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, int cap = 0) {
   const int64_t n_rt = (a.M + mx::kTM - 1) / mx::kTM, n_ct = (a.N + mx::kTC - 1) / mx::kTC;
   if (n_rt > INT32_MAX || n_ct > INT32_MAX) return MXFP8_ERR_OVERFLOW;
@@ -143,7 +146,8 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, in
   a.n_ct = (int32_t)n_ct;
   int64_t blocks, per;
   if (!mul_ok(n_rt, n_ct, &per) || per > UINT32_MAX || !mul_ok(per, batches, &blocks)) return MXFP8_ERR_OVERFLOW;
-  const void *k = rows ? (const void *)&mx::k_tiled<Op, true> : (const void *)&mx::k_tiled<Op, false>;
+  const void *k =
+      rows ? (const void *)&mx::k_tiled<Op, true, GROUPS> : (const void *)&mx::k_tiled<Op, false, GROUPS>;
   // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
   a.band = (int32_t)std::min<int64_t>(rows ? kBandBoth : kBandCol, n_rt);
   const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op>());
@@ -190,7 +194,20 @@ mxfp8_status dispatch_2d(const Args &a, int layout, void *stream) {
     return launch((const void *)&mx::k_rowwise<Op, kRowUnroll>, blocks, 256, a, stream);
   }
   const int64_t tiles = ((a.M + mx::kTM - 1) / mx::kTM) * ((a.N + mx::kTC - 1) / mx::kTC);
-  return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream, tiles >= kCapTiles2d ? 2 : 0);
+  const int cap = tiles >= kCapTiles2d ? 2 : 0;
+  if (a.n_grp > 0) return launch_colwise<Op, true>(a, layout == MXFP8_BOTH, 1, stream, cap);
+  return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream, cap);
+}
+
+// Checks of the token-group arguments of the grouped casts: 1..kMaxGroups
+// cumulative ends in device memory (4-byte aligned); token indices are
+// 32-bit in the kernel.
+mxfp8_status check_groups(const int32_t *group_ends, int64_t n_groups, int64_t M) {
+  if (n_groups < 1 || n_groups > mx::kMaxGroups) return MXFP8_ERR_SHAPE;
+  if (!group_ends) return MXFP8_ERR_NULL;
+  if (((uintptr_t)group_ends & 3u) != 0) return MXFP8_ERR_ALIGN;
+  if (M > INT32_MAX - 256) return MXFP8_ERR_OVERFLOW;
+  return MXFP8_OK;
 }
 
 Args make_args(const void *const *in, const int64_t *ld_in, int n_in, int64_t M, int64_t N, void *q_row,
@@ -214,21 +231,20 @@ Args make_args(const void *const *in, const int64_t *ld_in, int n_in, int64_t M,
   return a;
 }
 
-}  // namespace
 
-extern "C" {
-
-mxfp8_status mxfp8_gated_fwd(int act, const void *gate, int64_t ld_gate, const void *up, int64_t ld_up,
-                             int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
-                             int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
-                             void *stream) {
+mxfp8_status gated_fwd_impl(int act, const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
+                            int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row, int64_t ld_s_row,
+                            void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col, const int32_t *grp,
+                            int64_t n_grp, void *stream) {
   if (!act_ok(act)) return MXFP8_ERR_ACT;
   const void *in[2] = {gate, up};
   const int64_t ld[2] = {ld_gate, ld_up};
   mxfp8_status st = check_2d(Kind::Fwd, in, ld, 2, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
-                             ld_q_col, s_col, ld_s_col);
+                             ld_q_col, s_col, ld_s_col, n_grp);
   if (st != MXFP8_OK || M == 0 || N == 0) return st;
   Args a = make_args(in, ld, 2, M, N, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
+  a.grp = grp;
+  a.n_grp = (int32_t)n_grp;
   switch (act) {
     case MXFP8_ACT_SILU: return dispatch_2d<mx::OpFwd>(a, layout, stream);
     case MXFP8_ACT_GELU_TANH: return dispatch_2d<mx::GatedFwd<mx::ActGeluTanh>>(a, layout, stream);
@@ -237,23 +253,82 @@ mxfp8_status mxfp8_gated_fwd(int act, const void *gate, int64_t ld_gate, const v
   }
 }
 
-mxfp8_status mxfp8_gated_bwd(int act, const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate,
-                             const void *up, int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row,
-                             int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
-                             void *s_col, int64_t ld_s_col, void *stream) {
+mxfp8_status gated_bwd_impl(int act, const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate,
+                            const void *up, int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row,
+                            int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                            void *s_col, int64_t ld_s_col, const int32_t *grp, int64_t n_grp, void *stream) {
   if (!act_ok(act)) return MXFP8_ERR_ACT;
   const void *in[3] = {dh, gate, up};
   const int64_t ld[3] = {ld_dh, ld_gate, ld_up};
   mxfp8_status st = check_2d(Kind::Bwd, in, ld, 3, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
-                             ld_q_col, s_col, ld_s_col);
+                             ld_q_col, s_col, ld_s_col, n_grp);
   if (st != MXFP8_OK || M == 0 || N == 0) return st;
   Args a = make_args(in, ld, 3, M, N, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
+  a.grp = grp;
+  a.n_grp = (int32_t)n_grp;
   switch (act) {
     case MXFP8_ACT_SILU: return dispatch_2d<mx::OpBwd>(a, layout, stream);
     case MXFP8_ACT_GELU_TANH: return dispatch_2d<mx::GatedBwd<mx::ActGeluTanh>>(a, layout, stream);
     case MXFP8_ACT_GELU: return dispatch_2d<mx::GatedBwd<mx::ActGelu>>(a, layout, stream);
     default: return dispatch_2d<mx::GatedBwd<mx::ActRelu>>(a, layout, stream);
   }
+}
+
+mxfp8_status quant_2d_impl(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout, void *q_row,
+                           int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                           void *s_col, int64_t ld_s_col, const int32_t *grp, int64_t n_grp, void *stream) {
+  const void *in[1] = {x};
+  const int64_t ld[1] = {ld_x};
+  mxfp8_status st = check_2d(Kind::Quant, in, ld, 1, M, K, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
+                             ld_q_col, s_col, ld_s_col, n_grp);
+  if (st != MXFP8_OK || M == 0 || K == 0) return st;
+  Args a = make_args(in, ld, 1, M, K, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
+  a.grp = grp;
+  a.n_grp = (int32_t)n_grp;
+  return dispatch_2d<mx::OpQuant>(a, layout, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+mxfp8_status mxfp8_gated_fwd(int act, const void *gate, int64_t ld_gate, const void *up, int64_t ld_up,
+                             int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
+                             int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                             void *stream) {
+  return gated_fwd_impl(act, gate, ld_gate, up, ld_up, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
+                        ld_q_col, s_col, ld_s_col, nullptr, 0, stream);
+}
+
+mxfp8_status mxfp8_gated_bwd(int act, const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate,
+                             const void *up, int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row,
+                             int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                             void *s_col, int64_t ld_s_col, void *stream) {
+  return gated_bwd_impl(act, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout, q_row, ld_q_row, s_row, ld_s_row,
+                        q_col, ld_q_col, s_col, ld_s_col, nullptr, 0, stream);
+}
+
+mxfp8_status mxfp8_gated_fwd_grouped(int act, const void *gate, int64_t ld_gate, const void *up, int64_t ld_up,
+                                     int64_t M, int64_t N, int layout, void *q_row, int64_t ld_q_row, void *s_row,
+                                     int64_t ld_s_row, void *q_col, int64_t ld_q_col, void *s_col, int64_t ld_s_col,
+                                     const int32_t *group_ends, int64_t n_groups, void *stream) {
+  if (!act_ok(act)) return MXFP8_ERR_ACT;
+  mxfp8_status st = check_groups(group_ends, n_groups, M);
+  if (st != MXFP8_OK) return st;
+  return gated_fwd_impl(act, gate, ld_gate, up, ld_up, M, N, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
+                        ld_q_col, s_col, ld_s_col, group_ends, n_groups, stream);
+}
+
+mxfp8_status mxfp8_gated_bwd_grouped(int act, const void *dh, int64_t ld_dh, const void *gate, int64_t ld_gate,
+                                     const void *up, int64_t ld_up, int64_t M, int64_t N, int layout, void *q_row,
+                                     int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                                     void *s_col, int64_t ld_s_col, const int32_t *group_ends, int64_t n_groups,
+                                     void *stream) {
+  if (!act_ok(act)) return MXFP8_ERR_ACT;
+  mxfp8_status st = check_groups(group_ends, n_groups, M);
+  if (st != MXFP8_OK) return st;
+  return gated_bwd_impl(act, dh, ld_dh, gate, ld_gate, up, ld_up, M, N, layout, q_row, ld_q_row, s_row, ld_s_row,
+                        q_col, ld_q_col, s_col, ld_s_col, group_ends, n_groups, stream);
 }
 
 mxfp8_status mxfp8_swiglu_fwd(const void *gate, int64_t ld_gate, const void *up, int64_t ld_up, int64_t M,
@@ -275,13 +350,18 @@ mxfp8_status mxfp8_swiglu_bwd(const void *dh, int64_t ld_dh, const void *gate, i
 mxfp8_status mxfp8_quant_2d(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout, void *q_row,
                             int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
                             void *s_col, int64_t ld_s_col, void *stream) {
-  const void *in[1] = {x};
-  const int64_t ld[1] = {ld_x};
-  mxfp8_status st = check_2d(Kind::Quant, in, ld, 1, M, K, layout, q_row, ld_q_row, s_row, ld_s_row, q_col,
-                             ld_q_col, s_col, ld_s_col);
-  if (st != MXFP8_OK || M == 0 || K == 0) return st;
-  Args a = make_args(in, ld, 1, M, K, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col);
-  return dispatch_2d<mx::OpQuant>(a, layout, stream);
+  return quant_2d_impl(x, ld_x, M, K, layout, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col,
+                       nullptr, 0, stream);
+}
+
+mxfp8_status mxfp8_quant_2d_grouped(const void *x, int64_t ld_x, int64_t M, int64_t K, int layout, void *q_row,
+                                    int64_t ld_q_row, void *s_row, int64_t ld_s_row, void *q_col, int64_t ld_q_col,
+                                    void *s_col, int64_t ld_s_col, const int32_t *group_ends, int64_t n_groups,
+                                    void *stream) {
+  mxfp8_status st = check_groups(group_ends, n_groups, M);
+  if (st != MXFP8_OK) return st;
+  return quant_2d_impl(x, ld_x, M, K, layout, q_row, ld_q_row, s_row, ld_s_row, q_col, ld_q_col, s_col, ld_s_col,
+                       group_ends, n_groups, stream);
 }
 
 mxfp8_status mxfp8_quant_3d_colwise(const void *w, int64_t E, int64_t N, int64_t K, int64_t stride_e,
@@ -339,43 +419,60 @@ mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *ga
 
 namespace {
 
-// Checks and launch shared by the plain and grouped GEMM.  G == 0 is the
-// plain form (offsets unused, one expert).
-mxfp8_status gemm_launch(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b, int64_t ldb,
-                         int64_t stride_b, const void *sb, int64_t ld_sb, int64_t stride_sb, const int32_t *offs,
-                         int64_t G, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc, void *stream) {
+// Checks and launch shared by the three GEMM forms.  G == 0 is the plain
+// form (offsets unused, one expert); kGemmGroupM groups the rows of A (B per
+// group at b + g * stride_b); kGemmGroupK groups the contraction axis (C per
+// group at c + g * stride_c, scales in the per-group padded layout).
+mxfp8_status gemm_launch(int mode, const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b,
+                         int64_t ldb, int64_t stride_b, const void *sb, int64_t ld_sb, int64_t stride_sb,
+                         const int32_t *offs, int64_t G, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc,
+                         int64_t stride_c, void *stream) {
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || G < 0 || G > mx::kMaxGroups) return MXFP8_ERR_SHAPE;
   if (M == 0 || N == 0) return MXFP8_OK;
   if (!a || !sa || !b || !sb || !c || (G > 0 && !offs)) return MXFP8_ERR_NULL;
-  if (lda < K || ldb < K || lda % 16 != 0 || ldb % 16 != 0 || ld_sa < K / 32 || ld_sb < K / 32 || ldc < N)
+  // scale columns the operands reach: K/32, or with token groups the
+  // per-group padded layout, whose positions stay below K/32 + 16 G
+  const int64_t s_w = K / 32 + (mode == mx::kGemmGroupK ? 16 * G : 0);
+  if (lda < K || ldb < K || lda % 16 != 0 || ldb % 16 != 0 || ld_sa < s_w || ld_sb < s_w || ldc < N)
     return MXFP8_ERR_STRIDE;
-  if (G > 0) {
+  if (mode == mx::kGemmGroupM) {
     int64_t span_b, span_sb;
     if (!mul_ok(N - 1, ldb, &span_b) || !add_ok(span_b, K, &span_b) || !mul_ok(N - 1, ld_sb, &span_sb) ||
         !add_ok(span_sb, K / 32, &span_sb))
       return MXFP8_ERR_OVERFLOW;
     if (stride_b < span_b || stride_b % 16 != 0 || stride_sb < span_sb) return MXFP8_ERR_STRIDE;
   }
+  if (mode == mx::kGemmGroupK) {
+    int64_t span_c;
+    if (!mul_ok(M - 1, ldc, &span_c) || !add_ok(span_c, N, &span_c)) return MXFP8_ERR_OVERFLOW;
+    if (stride_c < span_c) return MXFP8_ERR_STRIDE;
+  }
   if (!aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3u) != 0 || ((uintptr_t)offs & 3u) != 0)
     return MXFP8_ERR_ALIGN;
-  if (!extent_ok(M, K, lda) || !extent_ok(N, K, ldb) || !extent_ok(M, K / 32, ld_sa) ||
-      !extent_ok(N, K / 32, ld_sb) || !extent_ok(M, N, ldc))
+  if (!extent_ok(M, K, lda) || !extent_ok(N, K, ldb) || !extent_ok(M, s_w, ld_sa) || !extent_ok(N, s_w, ld_sb) ||
+      !extent_ok(M, N, ldc))
     return MXFP8_ERR_OVERFLOW;
   if (G > 0) {
     int64_t e;
-    if (!mul_ok(G - 1, stride_b, &e) || e >= (INT64_MAX >> 2) || !mul_ok(G - 1, stride_sb, &e) ||
-        e >= (INT64_MAX >> 2))
+    if (mode == mx::kGemmGroupM &&
+        (!mul_ok(G - 1, stride_b, &e) || e >= (INT64_MAX >> 2) || !mul_ok(G - 1, stride_sb, &e) ||
+         e >= (INT64_MAX >> 2)))
+      return MXFP8_ERR_OVERFLOW;
+    if (mode == mx::kGemmGroupK && (!mul_ok(G - 1, stride_c, &e) || e >= (INT64_MAX >> 2)))
       return MXFP8_ERR_OVERFLOW;
   }
   // tile-relative offsets are 32-bit: 256 rows of either operand must span less than 2^32 bytes
   if (lda >= (int64_t(1) << 23) || ldb >= (int64_t(1) << 23) || ld_sa >= (int64_t(1) << 23) ||
       ld_sb >= (int64_t(1) << 23))
     return MXFP8_ERR_OVERFLOW;
-  // Grouped: an upper bound of row tiles, each group adding at most one
+  // M-grouped: an upper bound of row tiles, each group adding at most one
   // partial tile, so the host never reads the device-side offsets.
-  const int64_t tiles_m = (M + mx::kBM - 1) / mx::kBM + G, tiles_n = (N + mx::kBN - 1) / mx::kBN;
+  const int64_t tiles_m = (M + mx::kBM - 1) / mx::kBM + (mode == mx::kGemmGroupM ? G : 0);
+  const int64_t tiles_n = (N + mx::kBN - 1) / mx::kBN;
   int64_t blocks;
-  if (!mul_ok(tiles_m, tiles_n, &blocks) || blocks > (int64_t)INT32_MAX / mx::kGemmThreads) return MXFP8_ERR_OVERFLOW;
+  if (!mul_ok(tiles_m, tiles_n, &blocks) || (mode == mx::kGemmGroupK && !mul_ok(blocks, G, &blocks)) ||
+      blocks > (int64_t)INT32_MAX / mx::kGemmThreads)
+    return MXFP8_ERR_OVERFLOW;
   mx::GemmArgs g{};
   g.a = static_cast<const uint8_t *>(a);
   g.sa = static_cast<const uint8_t *>(sa);
@@ -396,9 +493,12 @@ mxfp8_status gemm_launch(const void *a, int64_t lda, const void *sa, int64_t ld_
   g.G = (int32_t)G;
   g.stride_b = stride_b;
   g.stride_sb = stride_sb;
+  g.stride_c = stride_c;
   g.scale_vec = aligned16(sa) && aligned16(sb) && ld_sa % 16 == 0 && ld_sb % 16 == 0 && stride_sb % 16 == 0;
   void *kargs[] = {&g};
-  const void *k = G > 0 ? (const void *)&mx::k_mx_gemm<true> : (const void *)&mx::k_mx_gemm<false>;
+  const void *k = mode == mx::kGemmGroupM   ? (const void *)&mx::k_mx_gemm<mx::kGemmGroupM>
+                  : mode == mx::kGemmGroupK ? (const void *)&mx::k_mx_gemm<mx::kGemmGroupK>
+                                            : (const void *)&mx::k_mx_gemm<mx::kGemmPlain>;
   hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(mx::kGemmThreads), kargs, 0, (hipStream_t)stream);
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }
@@ -410,7 +510,8 @@ extern "C" {
 mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b, int64_t ldb,
                         const void *sb, int64_t ld_sb, int64_t M, int64_t N, int64_t K, float *c, int64_t ldc,
                         void *stream) {
-  return gemm_launch(a, lda, sa, ld_sa, b, ldb, 0, sb, ld_sb, 0, nullptr, 0, M, N, K, c, ldc, stream);
+  return gemm_launch(mx::kGemmPlain, a, lda, sa, ld_sa, b, ldb, 0, sb, ld_sb, 0, nullptr, 0, M, N, K, c, ldc, 0,
+                     stream);
 }
 
 mxfp8_status mxfp8_grouped_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b,
@@ -418,8 +519,17 @@ mxfp8_status mxfp8_grouped_gemm(const void *a, int64_t lda, const void *sa, int6
                                 const int32_t *offsets, int64_t G, int64_t M, int64_t N, int64_t K, float *c,
                                 int64_t ldc, void *stream) {
   if (G <= 0) return G == 0 ? MXFP8_OK : MXFP8_ERR_SHAPE;
-  return gemm_launch(a, lda, sa, ld_sa, b, ldb, stride_b, sb, ld_sb, stride_sb, offsets, G, M, N, K, c, ldc,
-                     stream);
+  return gemm_launch(mx::kGemmGroupM, a, lda, sa, ld_sa, b, ldb, stride_b, sb, ld_sb, stride_sb, offsets, G, M, N,
+                     K, c, ldc, 0, stream);
+}
+
+mxfp8_status mxfp8_grouped_gemm_k(const void *a, int64_t lda, const void *sa, int64_t ld_sa, const void *b,
+                                  int64_t ldb, const void *sb, int64_t ld_sb, const int32_t *group_ends, int64_t G,
+                                  int64_t M, int64_t N, int64_t T, float *c, int64_t ldc, int64_t stride_c,
+                                  void *stream) {
+  if (G <= 0) return G == 0 ? MXFP8_OK : MXFP8_ERR_SHAPE;
+  return gemm_launch(mx::kGemmGroupK, a, lda, sa, ld_sa, b, ldb, 0, sb, ld_sb, 0, group_ends, G, M, N, T, c, ldc,
+                     stride_c, stream);
 }
 
 const char *mxfp8_status_str(mxfp8_status status) {

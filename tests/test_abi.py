@@ -30,7 +30,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert names == {"mxfp8_swiglu_fwd", "mxfp8_swiglu_bwd", "mxfp8_gated_fwd", "mxfp8_gated_bwd",
                      "mxfp8_quant_2d", "mxfp8_quant_3d_colwise", "mxfp8_swiglu_fwd_bf16", "mxfp8_swiglu_bwd_bf16",
-                     "mxfp8_gemm", "mxfp8_grouped_gemm", "mxfp8_status_str"}
+                     "mxfp8_gemm", "mxfp8_grouped_gemm", "mxfp8_status_str", "mxfp8_gated_fwd_grouped",
+                     "mxfp8_gated_bwd_grouped", "mxfp8_quant_2d_grouped", "mxfp8_grouped_gemm_k"}
     for n in names:
         assert getattr(lib, n) is not None
 
@@ -294,6 +295,64 @@ def test_grouped_gemm_errors():
     assert ggemm(offs=A + 2) == ALIGN
     assert ggemm(lda=120) == STRIDE
     assert ggemm(M=0, a=None) == OK
+
+
+def kgemm(**kw):
+    a = dict(a=A, lda=256, sa=A, ld_sa=8 + 48, b=A, ldb=256, sb=A, ld_sb=8 + 48, offs=A, G=3, M=64, N=48, T=256,
+             c=A, ldc=48, stride_c=64 * 48)
+    a.update(kw)
+    return mx.lib().mxfp8_grouped_gemm_k(a["a"], a["lda"], a["sa"], a["ld_sa"], a["b"], a["ldb"], a["sb"], a["ld_sb"],
+                                         a["offs"], a["G"], a["M"], a["N"], a["T"], a["c"], a["ldc"], a["stride_c"],
+                                         None)
+
+
+def test_grouped_gemm_k_errors():
+    assert kgemm(G=0, offs=None) == OK                # no groups: nothing to do
+    assert kgemm(G=-1) == SHAPE
+    assert kgemm(G=1025) == SHAPE
+    assert kgemm(T=240) == SHAPE                      # tokens not a multiple of 32
+    assert kgemm(offs=None) == NULL
+    assert kgemm(ld_sa=8 + 47) == STRIDE              # padded scale rows need T/32 + 16 G
+    assert kgemm(ld_sb=8 + 47) == STRIDE
+    assert kgemm(lda=248) == STRIDE
+    assert kgemm(stride_c=63 * 48) == STRIDE          # group results would overlap
+    assert kgemm(offs=A + 2) == ALIGN
+    assert kgemm(c=A + 2) == ALIGN
+    assert kgemm(M=0, a=None) == OK
+
+
+def grouped_cast(fn, **kw):
+    lib = mx.lib()
+    a = dict(gate=A, ld_gate=256, up=A + 256, ld_up=256, dh=A, ld_dh=128, M=64, N=128, layout=3,
+             q_row=A, ld_q_row=256, s_row=A, ld_s_row=8, q_col=A, ld_q_col=64, s_col=A, ld_s_col=2 + 16 * 2,
+             offs=A, G=2, act=0)
+    a.update(kw)
+    common = (a["M"], a["N"], a["layout"], a["q_row"], a["ld_q_row"], a["s_row"], a["ld_s_row"], a["q_col"],
+              a["ld_q_col"], a["s_col"], a["ld_s_col"], a["offs"], a["G"], None)
+    if fn == "fwd":
+        return lib.mxfp8_gated_fwd_grouped(a["act"], a["gate"], a["ld_gate"], a["up"], a["ld_up"], *common)
+    if fn == "bwd":
+        return lib.mxfp8_gated_bwd_grouped(a["act"], a["dh"], a["ld_dh"], a["gate"], a["ld_gate"], a["up"],
+                                           a["ld_up"], *common)
+    return lib.mxfp8_quant_2d_grouped(a["gate"], a["ld_gate"], *common)
+
+
+@pytest.mark.parametrize("fn", ["fwd", "bwd", "quant"])
+def test_grouped_cast_errors(fn):
+    """The token-group checks come on top of the ungrouped casts' checks;
+    colwise scale rows must hold M/32 + 16 groups."""
+    assert grouped_cast(fn, G=0) == SHAPE
+    assert grouped_cast(fn, G=1025) == SHAPE
+    assert grouped_cast(fn, offs=None) == NULL
+    assert grouped_cast(fn, offs=A + 2) == ALIGN
+    assert grouped_cast(fn, ld_s_col=2 + 16 * 2 - 1) == STRIDE
+    # rowwise only: the colwise scale row is not checked (the call fails on
+    # the NULL input instead, before any launch)
+    assert grouped_cast(fn, layout=1, ld_s_col=0, gate=None, dh=None) == NULL
+    assert grouped_cast(fn, M=1 << 31, ld_q_col=1 << 31) == OVERFLOW
+    if fn != "quant":
+        assert grouped_cast(fn, act=9) == ACT
+    assert grouped_cast(fn, M=0) == OK
 
 
 def test_stream_probe_exports_and_checks():
