@@ -429,6 +429,7 @@ from swiglu_activation_cast_amd.metrics import STREAM_CONFIGS  # noqa: E402
 STREAM_MIXES = {"4:1": (4, 1), "2:1": (2, 1), "3:1": (3, 1), "3:2": (3, 2), "1:1": (1, 1)}
 CALL_MIX = {"fwd_row": "4:1", "fwd_col": "4:1", "fwd_both": "2:1", "bwd_row": "3:1", "bwd_col": "3:1",
             "bwd_both": "3:2", "quant2d_row": "2:1", "quant2d_col": "2:1", "quant3d_E64": "2:1",
+            "bwd_both_grouped_g8": "3:2", "quant2d_col_grouped_g8": "2:1",
             **{f"{a}_{d}_both": m for a in ("gelu_tanh", "gelu", "relu") for d, m in (("fwd", "2:1"), ("bwd", "3:2"))}}
 
 
@@ -565,7 +566,49 @@ def run_detail(inp, fwd_out, bwd_out, stream):
     tflops = 2.0 * gm * gn * gk / avg / 1e12
     res["grouped_gemm_16640x8192x5120_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
                                               "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
-    del qa, qb, sa, sb, qb3, sb3, cg, offs
+    del qa, qb, sa, sb, qb3, sb3, cg
+    torch.cuda.empty_cache()
+    # the input gradient at the same shape, its expert operand the 3D cast's
+    # output as written: dx [16640, 5120] = dy [16640, 8192] W_g [8192, 5120]
+    dy = synth.normal_bf16((gm, gn), 1.0, seed=74, device=inp.gate.device)
+    w3 = synth.expert_weights(ng, gn, gk, seed=75, std=0.02, device=inp.gate.device)
+    qa, _, sa, _ = mx.mxfp8_quant_2d(dy, rowwise=True, stream=stream)
+    q3, s3 = mx.mxfp8_quant_3d_colwise(w3, stream=stream)
+    del w3
+    cg = torch.empty((gm, gk), dtype=torch.float32, device=inp.gate.device)
+    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm(qa, sa, q3, s3, offs, out=cg, stream=stream), 20, 10)
+    tflops = 2.0 * gm * gn * gk / avg / 1e12
+    res["dgrad_grouped_gemm_16640x5120x8192_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
+                                                    "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+    del qa, sa, q3, s3, cg
+    # the weight gradient: dW_g [8192, 5120] = dy_g^T x_g over each expert's
+    # tokens, operands the grouped colwise casts (per-group padded scales)
+    x = synth.normal_bf16((gm, gk), 1.0, seed=76, device=inp.gate.device)
+    _, qa, _, sa = mx.mxfp8_quant_2d_grouped(dy, offs, stream=stream)
+    _, qb, _, sb = mx.mxfp8_quant_2d_grouped(x, offs, stream=stream)
+    del dy, x
+    cw = torch.empty((ng, gn, gk), dtype=torch.float32, device=inp.gate.device)
+    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm_k(qa, sa, qb, sb, offs, out=cw, stream=stream), 20, 10)
+    tflops = 2.0 * gm * gn * gk / avg / 1e12
+    res["wgrad_grouped_gemm_k_8192x5120_t16640_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
+                                                       "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+    del qa, sa, qb, sb, cw, offs
+    torch.cuda.empty_cache()
+    # the grouped casts at 131072 x 8192 (8 token groups): colwise scales in
+    # the per-group padded layout, the same bytes as the plain casts
+    ends = torch.arange(1, 9, dtype=torch.int32, device=inp.gate.device) * (M // 8)
+    bo = mx.alloc_outputs(M, 2 * N, mx.BOTH, inp.gate.device, 8)
+    qo = mx.alloc_outputs(M, N, mx.COLWISE, inp.gate.device, 8)
+    for name, fn, nbytes in (
+            ("bwd_both_grouped_g8", lambda: mx.mxfp8_gated_bwd_grouped(inp.dh, inp.gate, inp.up, ends, out=bo,
+                                                                        stream=stream),
+             metrics.swiglu_bwd_bytes(M, N, mx.BOTH)),
+            ("quant2d_col_grouped_g8", lambda: mx.mxfp8_quant_2d_grouped(inp.dh, ends, out=qo, stream=stream),
+             metrics.quant_2d_bytes(M, N, mx.COLWISE))):
+        avg, _ = time_launches(fn, 10, 2)
+        res[name] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nbytes, avg), 1),
+                     "frac": round(metrics.gbps(nbytes, avg) / metrics.HBM_PEAK_GBPS, 4)}
+    del bo, qo, ends
     torch.cuda.empty_cache()
     # 3D expert cast, 64 experts of 8192 x 5120 (inputs 5.4 GB)
     w = synth.expert_workload(64, device=inp.gate.device)

@@ -22,7 +22,7 @@ from __future__ import annotations
 
 import numpy as np
 
-DEGREE = {"P": 9, "Q": 10}
+DEGREE = {"P": 8, "Q": 8}
 NODES = 40001
 
 

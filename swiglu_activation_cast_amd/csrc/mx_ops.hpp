@@ -121,19 +121,16 @@ struct ActGeluTanh {
 // with t = 2 / (2 + z) and x = 2t - 1: the change of variable of
 // Schonfelder's Chebyshev expansions of the error function, which maps z in
 // [0, inf) onto x in (-1, 1], where Q(x) = erfcx(z) (2 + z) / 2 and
-// P(x) = ln Q(x) are smooth.  P (degree 9) and Q (degree 10) are the
-// least-squares fits printed by gen_erfc_fit.py (fit errors 1.0e-7 and
-// 1.2e-8, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
+// P(x) = ln Q(x) are smooth.  P and Q (degree 8 each) are the
+// least-squares fits printed by gen_erfc_fit.py (fit errors 1.4e-6 and
+// 7.9e-7, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
 // exact for a bf16 g.  The forward forms e^(-z^2 + P) with one exponential;
 // the backward forms e^(-z^2) once for both the cdf (times Q) and the
 // Gaussian of the derivative.  Phi(g) is erfc(z) / 2 for g < 0 and
 // 1 - erfc(z) / 2 otherwise.  For g < -8 the exponentials are formed times
 // 2^64 (2^-64 applied last).
-constexpr float kErfcP[10] = {-0x1.57f564p-1f, 0x1.58649p-1f, 0x1.83d5bp-5f, -0x1.7fffc4p-5f, -0x1.438b2ep-7f,
-                              0x1.1d34dep-7f, 0x1.d1b74cp-10f, -0x1.0c8826p-9f, -0x1.b404a2p-13f, 0x1.5df29ep-12f};
-constexpr float kErfcQ[11] = {0x1.058672p-1f,  0x1.5fd384p-2f,   0x1.1e2dc4p-3f,  0x1.2a8b38p-6f,
-                              -0x1.604f2ep-7f, -0x1.a9203p-9f,   0x1.90dcp-10f,   0x1.c39742p-12f,
-                              -0x1.39ececp-12f, -0x1.330a0ap-15f, 0x1.61ac72p-15f};
+constexpr float kErfcP[9] = {-0x1.57f564p-1f, 0x1.586306p-1f, 0x1.83d5bp-5f, -0x1.7eb7bp-5f, -0x1.438b1ep-7f, 0x1.0ac094p-7f, 0x1.d1b65p-10f, -0x1.5437d4p-10f, -0x1.b40028p-13f};
+constexpr float kErfcQ[9] = {0x1.058674p-1f, 0x1.5fd3dcp-2f, 0x1.1e2b9cp-3f, 0x1.2a4342p-6f, -0x1.5f3aep-7f, -0x1.a107bp-9f, 0x1.78aed2p-10f, 0x1.6d3c8p-12f, -0x1.96ce9p-13f};
 
 struct ActGelu {
   static constexpr float kRsqrt2 = 0.7071067811865476f;
@@ -146,9 +143,9 @@ struct ActGelu {
   __device__ __forceinline__ static float half_erfc(float g) {
     const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
     const float x = __builtin_fmaf(th, 4.0f, -1.0f);
-    float p = kErfcP[9];
+    float p = kErfcP[8];
 #pragma unroll
-    for (int i = 8; i >= 0; i--) p = __builtin_fmaf(p, x, kErfcP[i]);
+    for (int i = 7; i >= 0; i--) p = __builtin_fmaf(p, x, kErfcP[i]);
     const float e = __builtin_fmaf(-0.5f * g, g, p);  // -z^2 + P(x)
     return th * __builtin_amdgcn_exp2f(scaled ? __builtin_fmaf(e, kLog2e, 64.0f) : e * kLog2e);
   }
@@ -162,9 +159,9 @@ struct ActGelu {
   __device__ __forceinline__ static float half_erfc_q(float g, float e) {
     const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
     const float x = __builtin_fmaf(th, 4.0f, -1.0f);
-    float q = kErfcQ[10];
+    float q = kErfcQ[8];
 #pragma unroll
-    for (int i = 9; i >= 0; i--) q = __builtin_fmaf(q, x, kErfcQ[i]);
+    for (int i = 7; i >= 0; i--) q = __builtin_fmaf(q, x, kErfcQ[i]);
     return (th * q) * e;
   }
   __device__ __forceinline__ static float cdf_q(float g, float e) {
@@ -256,23 +253,18 @@ template <class Act>
 struct GatedBwd {
   static constexpr int IN = 3, OUT = 2;  // in: dh, gate, up; out: dgate, dup
 
-  template <bool careful>
-  __device__ __forceinline__ static void elem(float dhv, float gv, float uv, float &dg, float &du) {
-    const float a = round_bf16(Act::template bwd_act<careful>(gv));
-    du = dhv * a;
-    const float da = round_bf16(dhv * uv);
-    dg = Act::template dgate<careful>(da, gv);
-  }
-
+  // One packed word (two elements): a = bf16(act(g)), du = bf16(dh a),
+  // da = bf16(dh u), dg = bf16(da act'(g)); each bf16 rounding takes both
+  // elements of the pair in one convert.
   template <bool careful>
   __device__ __forceinline__ static void eval(const u32 *dh, const u32 *g, const u32 *u, u32 *dg, u32 *du) {
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      float g0, u0, g1, u1;
-      elem<careful>(lo_f(dh[k]), lo_f(g[k]), lo_f(u[k]), g0, u0);
-      elem<careful>(hi_f(dh[k]), hi_f(g[k]), hi_f(u[k]), g1, u1);
-      dg[k] = pack_bf16(g0, g1);
-      du[k] = pack_bf16(u0, u1);
+      const float g0 = lo_f(g[k]), g1 = hi_f(g[k]), h0 = lo_f(dh[k]), h1 = hi_f(dh[k]);
+      const u32 ap = pack_bf16(Act::template bwd_act<careful>(g0), Act::template bwd_act<careful>(g1));
+      du[k] = pack_bf16(h0 * lo_f(ap), h1 * hi_f(ap));
+      const u32 dap = pack_bf16(h0 * lo_f(u[k]), h1 * hi_f(u[k]));
+      dg[k] = pack_bf16(Act::template dgate<careful>(lo_f(dap), g0), Act::template dgate<careful>(hi_f(dap), g1));
     }
   }
 

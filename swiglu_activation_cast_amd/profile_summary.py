@@ -68,23 +68,36 @@ def bench_calls(workload: str, experts: int):
             if lay == 1:
                 pat, grid = f"k_rowwise<mx::Op{op},", rows
             else:
-                pat, grid = f"k_tiled<mx::Op{op}, {'true' if lay == 3 else 'false'}>", _tiles(M, N)
+                pat, grid = f"k_tiled<mx::Op{op}, {'true' if lay == 3 else 'false'}, false>", _tiles(M, N)
             calls.append(Call(pat, f"{op.lower()}_{name}", rd, fn(M, N, lay) - rd, grid))
     for act in ("GeluTanh", "Gelu", "Relu"):
         label = {"GeluTanh": "gelu_tanh", "Gelu": "gelu", "Relu": "relu"}[act]
         for op, fn, rd in (("Fwd", metrics.swiglu_fwd_bytes, 4 * M * N), ("Bwd", metrics.swiglu_bwd_bytes, 6 * M * N)):
-            calls.append(Call(f"k_tiled<mx::Gated{op}<mx::Act{act}>, true>", f"{label}_{op.lower()}_both", rd,
+            calls.append(Call(f"k_tiled<mx::Gated{op}<mx::Act{act}>, true, false>", f"{label}_{op.lower()}_both", rd,
                               fn(M, N, 3) - rd, _tiles(M, N)))
     calls += [
         Call("k_rowwise<mx::OpQuant,", "quant2d_row", 2 * M * N, one, rows),
-        Call("k_tiled<mx::OpQuant, false>", "quant2d_col", 2 * M * N, one, _tiles(M, N)),
-        Call("k_tiled<mx::OpQuant, false>", f"quant3d_E{E}", 2 * E * N3 * K3,
+        Call("k_tiled<mx::OpQuant, false, false>", "quant2d_col", 2 * M * N, one, _tiles(M, N)),
+        Call("k_tiled<mx::OpQuant, false, false>", f"quant3d_E{E}", 2 * E * N3 * K3,
              metrics.quant_3d_bytes(E, N3, K3) - 2 * E * N3 * K3, _tiles(N3, K3, E)),
+        Call("k_tiled<mx::OpBwd, true, true>", "bwd_both_grouped_g8", 6 * M * N,
+             metrics.swiglu_bwd_bytes(M, N, 3) - 6 * M * N, _tiles(M, N)),
+        Call("k_tiled<mx::OpQuant, false, true>", "quant2d_col_grouped_g8", 2 * M * N, one, _tiles(M, N)),
         Call("k_values<mx::OpFwd,", "unfused_fwd_values", 4 * M * N, 2 * M * N, rows),
         Call("k_values<mx::OpBwd,", "unfused_bwd_values", 6 * M * N, 4 * M * N, rows),
-        Call("k_tiled<mx::OpQuant, true>", "unfused_fwd_quant_both", 2 * M * N, 2 * one, _tiles(M, N)),
-        Call("k_tiled<mx::OpQuant, true>", "unfused_bwd_quant_both", 4 * M * N, 4 * one, _tiles(M, 2 * N)),
+        Call("k_tiled<mx::OpQuant, true, false>", "unfused_fwd_quant_both", 2 * M * N, 2 * one, _tiles(M, N)),
+        Call("k_tiled<mx::OpQuant, true, false>", "unfused_bwd_quant_both", 4 * M * N, 4 * one, _tiles(M, 2 * N)),
     ]
+    # the MX GEMM consumer (bytes: the operands and C once; it is bound by
+    # the matrix cores, and the rows give its duration per call)
+    for label, mode, gm, gn, gk, G in (("gemm_16384x8192x5120", 0, 16384, 8192, 5120, 0),
+                                       ("grouped_gemm_16640x8192x5120_g4", 1, 16640, 8192, 5120, 4),
+                                       ("dgrad_grouped_gemm_16640x5120x8192_g4", 1, 16640, 5120, 8192, 4),
+                                       ("wgrad_grouped_gemm_k_8192x5120_t16640_g4", 2, 8192, 5120, 16640, 4)):
+        tiles_m = -(-gm // 256) + (G if mode == 1 else 0)
+        grid = tiles_m * -(-gn // 256) * (G if mode == 2 else 1)
+        rd = gm * gk + gn * gk * (G if mode == 1 else 1)
+        calls.append(Call(f"k_mx_gemm<{mode}>", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid))
     gib = COPY_BYTES
     for mix, (nr, nw) in (("4:1", (4, 1)), ("2:1", (2, 1)), ("3:1", (3, 1)), ("3:2", (3, 2)), ("1:1", (1, 1))):
         for u, grid in STREAM_CONFIGS:

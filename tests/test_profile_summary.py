@@ -36,10 +36,10 @@ def _fake(tmp_path):
     bwd, q2, q3 = c["bwd_both"], c["quant2d_col"], c["quant3d_E64"]
     copy = "void (anonymous namespace)::k_stream<1, 1, 8>((anonymous namespace)::StreamArgs)"
     seq = [
-        ("void mx::k_tiled<mx::OpBwd, true>(mx::Args)", bwd.grid, bwd.read / 2 / kib, bwd.write * 1.08 / kib),
-        ("void mx::k_tiled<mx::OpBwd, true>(mx::Args)", bwd.grid, bwd.read / 2 / kib, bwd.write * 1.08 / kib),
-        ("void mx::k_tiled<mx::OpQuant, false>(mx::Args)", q2.grid, q2.read / 2 / kib, q2.write / kib),
-        ("void mx::k_tiled<mx::OpQuant, false>(mx::Args)", q3.grid, q3.read / 2 / kib, q3.write * 1.01 / kib),
+        ("void mx::k_tiled<mx::OpBwd, true, false>(mx::Args)", bwd.grid, bwd.read / 2 / kib, bwd.write * 1.08 / kib),
+        ("void mx::k_tiled<mx::OpBwd, true, false>(mx::Args)", bwd.grid, bwd.read / 2 / kib, bwd.write * 1.08 / kib),
+        ("void mx::k_tiled<mx::OpQuant, false, false>(mx::Args)", q2.grid, q2.read / 2 / kib, q2.write / kib),
+        ("void mx::k_tiled<mx::OpQuant, false, false>(mx::Args)", q3.grid, q3.read / 2 / kib, q3.write * 1.01 / kib),
         (copy, 4096, ps.COPY_BYTES / 2 / kib, ps.COPY_BYTES / kib),
         (copy, 2048, ps.COPY_BYTES / 2 / kib, ps.COPY_BYTES / kib),
         (copy, 8192, ps.COPY_BYTES / 2 / kib, ps.COPY_BYTES / kib),
@@ -57,7 +57,7 @@ def test_calls_have_distinct_keys():
         key = (c.pattern, c.grid)
         assert key not in keys, (c.label, keys.get(key))
         keys[key] = c.label
-    assert ps._match(ps.bench_calls(W, 64), "void mx::k_tiled<mx::OpQuant, false>(mx::Args)",
+    assert ps._match(ps.bench_calls(W, 64), "void mx::k_tiled<mx::OpQuant, false, false>(mx::Args)",
                      _calls()["quant3d_E64"].grid * ps.THREADS).label == "quant3d_E64"
 
 
@@ -77,8 +77,8 @@ def test_traffic_summary(tmp_path):
 
 
 def test_traffic_needs_the_copy(tmp_path):
-    _write(str(tmp_path / "f"), "FETCH_SIZE", [("void mx::k_tiled<mx::OpBwd, true>(mx::Args)", 65536, 1.0)])
-    _write(str(tmp_path / "w"), "WRITE_SIZE", [("void mx::k_tiled<mx::OpBwd, true>(mx::Args)", 65536, 1.0)])
+    _write(str(tmp_path / "f"), "FETCH_SIZE", [("void mx::k_tiled<mx::OpBwd, true, false>(mx::Args)", 65536, 1.0)])
+    _write(str(tmp_path / "w"), "WRITE_SIZE", [("void mx::k_tiled<mx::OpBwd, true, false>(mx::Args)", 65536, 1.0)])
     with pytest.raises(SystemExit):
         ps.traffic(str(tmp_path / "f"), str(tmp_path / "w"), W, 64, [], str(tmp_path / "o"))
 
@@ -90,7 +90,7 @@ def test_stats_per_call(tmp_path):
     t = 1000
     for grid, dur in ((c["quant2d_col"].grid, 500_000), (c["quant3d_E64"].grid, 1_400_000),
                       (c["quant2d_col"].grid, 520_000), (c["quant3d_E64"].grid, 1_420_000), (77, 5_000)):
-        rows.append({"Kernel_Name": "void mx::k_tiled<mx::OpQuant, false>(mx::Args)", "Grid_Size_X": grid * 256,
+        rows.append({"Kernel_Name": "void mx::k_tiled<mx::OpQuant, false, false>(mx::Args)", "Grid_Size_X": grid * 256,
                      "Grid_Size_Y": 1, "Start_Timestamp": t, "End_Timestamp": t + dur})
         t += dur + 10
     p = tmp_path / "k.csv"
@@ -113,8 +113,8 @@ def test_counters_mean_and_derived_figures(tmp_path):
     derived matrix-core utilization and L2 hit rate (invented values: 8 XCDs
     of 1000 active cycles each, 1024 SIMDs busy 250 cycles each -> 25 %; 90
     hits, 10 misses -> 90 %)."""
-    k = "void mx::k_mx_gemm<false>(mx::GemmArgs)"
-    other = "void mx::k_tiled<mx::OpBwd, true>(mx::Args)"
+    k = "void mx::k_mx_gemm<0>(mx::GemmArgs)"
+    other = "void mx::k_tiled<mx::OpBwd, true, false>(mx::Args)"
     rows = []
     for name, grid, counter, vals in ((k, 2048, "SQ_VALU_MFMA_BUSY_CYCLES", (256000.0, 256000.0)),
                                       (k, 2048, "GRBM_GUI_ACTIVE", (8000.0, 8000.0)),
@@ -131,7 +131,7 @@ def test_counters_mean_and_derived_figures(tmp_path):
             w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Grid_Size": grid * 256, "Counter_Name": counter,
                         "Counter_Value": v})
     out = tmp_path / "o.txt"
-    ps.counters([str(d)], "k_mx_gemm<false>", ["cmd"], str(out), grid=2048)
+    ps.counters([str(d)], "k_mx_gemm<0>", ["cmd"], str(out), grid=2048)
     text = out.read_text()
     assert "matrix-core utilization: 25.0%" in text
     assert "L2 hit rate: 90.0%" in text
