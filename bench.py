@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--cpu-slabs-1t", type=int, default=48, help="slabs for the single-thread oracle figure")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-detail", action="store_true", help="skip the per-op breakdown")
+    p.add_argument("--detail-set", choices=("full", "core"), default="full",
+                   help="core: only the per-layout casts, the gated casts and the streaming ceilings "
+                        "(shorter runs under counter collection)")
     p.add_argument("--validate-slabs", type=int, default=64,
                    help="random 32-row slabs checked against the oracle before timing (0: none)")
     p.add_argument("--sweep", action="store_true", help="print the per-shape table instead of the JSON line")
@@ -379,7 +382,7 @@ def main():
 
     detail = {}
     if not args.no_detail:
-        detail = run_detail(inp, fwd_out, bwd_out, stream)
+        detail = run_detail(inp, fwd_out, bwd_out, stream, core_only=args.detail_set == "core")
         mix = CALL_MIX["bwd_both" if dom_bytes == bwd_bytes else "fwd_both"]
         ceil = detail["stream_ceilings"][mix]["GB/s"]
         roofline["stream_ceiling"] = {"mix": mix, "GB/s": ceil, "frac_of_ceiling": round(achieved / ceil, 4)}
@@ -462,7 +465,7 @@ def stream_ceilings(inp, bwd_out, stream):
     return res
 
 
-def run_detail(inp, fwd_out, bwd_out, stream):
+def run_detail(inp, fwd_out, bwd_out, stream, core_only=False):
     """Each op and layout alone at the same size, the 3D expert cast, and a
     device copy of the w13 tensor as a bandwidth ceiling."""
     import torch
@@ -494,6 +497,9 @@ def run_detail(inp, fwd_out, bwd_out, stream):
             res[f"{act}_{op}_both"] = {"us": round(avg * 1e6, 2), "GB/s": round(metrics.gbps(nbytes, avg), 1),
                                        "frac": round(metrics.gbps(nbytes, avg) / metrics.HBM_PEAK_GBPS, 4)}
     print("bench: gated activations done", file=sys.stderr, flush=True)
+    if core_only:
+        res["stream_ceilings"] = stream_ceilings(inp, bwd_out, stream)
+        return res
     # the unfused two-kernel pipeline (bf16 activation written, then the plain
     # cast of it), both layouts: the pages' baseline structure
     h = torch.empty((M, N), dtype=torch.bfloat16, device=inp.gate.device)

@@ -121,16 +121,19 @@ struct ActGeluTanh {
 // with t = 2 / (2 + z) and x = 2t - 1: the change of variable of
 // Schonfelder's Chebyshev expansions of the error function, which maps z in
 // [0, inf) onto x in (-1, 1], where Q(x) = erfcx(z) (2 + z) / 2 and
-// P(x) = ln Q(x) are smooth.  P and Q (degree 8 each) are the
-// least-squares fits printed by gen_erfc_fit.py (fit errors 1.4e-6 and
-// 7.9e-7, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
+// P(x) = ln Q(x) are smooth.  Both are evaluated in u = x - 1 = 2t - 2 as
+// P = u R_P(u) and Q = 1 + u R_Q(u), so that erfc(0) = 1 exactly whatever the
+// float32 rounding (tiny gates give the cdf 1/2 exactly, as the definition
+// does).  R_P and R_Q (degree 7, so P and Q have degree 8) are the
+// least-squares fits printed by gen_erfc_fit.py (fit errors 1.5e-6 and
+// 9.9e-7, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
 // exact for a bf16 g.  The forward forms e^(-z^2 + P) with one exponential;
 // the backward forms e^(-z^2) once for both the cdf (times Q) and the
 // Gaussian of the derivative.  Phi(g) is erfc(z) / 2 for g < 0 and
 // 1 - erfc(z) / 2 otherwise.  For g < -8 the exponentials are formed times
 // 2^64 (2^-64 applied last).
-constexpr float kErfcP[9] = {-0x1.57f564p-1f, 0x1.586306p-1f, 0x1.83d5bp-5f, -0x1.7eb7bp-5f, -0x1.438b1ep-7f, 0x1.0ac094p-7f, 0x1.d1b65p-10f, -0x1.5437d4p-10f, -0x1.b40028p-13f};
-constexpr float kErfcQ[9] = {0x1.058674p-1f, 0x1.5fd3dcp-2f, 0x1.1e2b9cp-3f, 0x1.2a4342p-6f, -0x1.5f3aep-7f, -0x1.a107bp-9f, 0x1.78aed2p-10f, 0x1.6d3c8p-12f, -0x1.96ce9p-13f};
+constexpr float kErfcP[8] = {0x1.41b1eep-1f, -0x1.3ad8b8p-4f, -0x1.a4d58ep-6f, -0x1.702f1ep-10f, -0x1.384eb8p-6f, -0x1.9bf628p-7f, -0x1.6f3c04p-9f, -0x1.8cb4e6p-13f};
+constexpr float kErfcQ[8] = {0x1.41bb3ap-1f, 0x1.f23f3cp-4f, -0x1.b16f94p-6f, -0x1.ab2da4p-8f, 0x1.e1a0cap-10f, -0x1.9fa6d2p-10f, -0x1.3db0bcp-10f, -0x1.98ded8p-13f};
 
 struct ActGelu {
   static constexpr float kRsqrt2 = 0.7071067811865476f;
@@ -142,11 +145,11 @@ struct ActGelu {
   template <bool scaled>
   __device__ __forceinline__ static float half_erfc(float g) {
     const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
-    const float x = __builtin_fmaf(th, 4.0f, -1.0f);
-    float p = kErfcP[8];
+    const float u = __builtin_fmaf(th, 4.0f, -2.0f);                              // x - 1
+    float r = kErfcP[7];
 #pragma unroll
-    for (int i = 7; i >= 0; i--) p = __builtin_fmaf(p, x, kErfcP[i]);
-    const float e = __builtin_fmaf(-0.5f * g, g, p);  // -z^2 + P(x)
+    for (int i = 6; i >= 0; i--) r = __builtin_fmaf(r, u, kErfcP[i]);
+    const float e = __builtin_fmaf(-0.5f * g, g, u * r);  // -z^2 + P(x)
     return th * __builtin_amdgcn_exp2f(scaled ? __builtin_fmaf(e, kLog2e, 64.0f) : e * kLog2e);
   }
 
@@ -158,11 +161,11 @@ struct ActGelu {
   // erfc(|g| / sqrt 2) / 2 from e = e^(-g^2/2) (times 2^64 if e is)
   __device__ __forceinline__ static float half_erfc_q(float g, float e) {
     const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
-    const float x = __builtin_fmaf(th, 4.0f, -1.0f);
-    float q = kErfcQ[8];
+    const float u = __builtin_fmaf(th, 4.0f, -2.0f);                              // x - 1
+    float r = kErfcQ[7];
 #pragma unroll
-    for (int i = 7; i >= 0; i--) q = __builtin_fmaf(q, x, kErfcQ[i]);
-    return (th * q) * e;
+    for (int i = 6; i >= 0; i--) r = __builtin_fmaf(r, u, kErfcQ[i]);
+    return (th * __builtin_fmaf(u, r, 1.0f)) * e;  // t/2 Q(x) e^(-z^2)
   }
   __device__ __forceinline__ static float cdf_q(float g, float e) {
     const float q = half_erfc_q(g, e);
