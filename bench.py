@@ -589,16 +589,20 @@ def run_detail(inp, fwd_out, bwd_out, stream, core_only=False):
     del qa, sa, q3, s3, cg
     # the weight gradient: dW_g [8192, 5120] = dy_g^T x_g over each expert's
     # tokens, operands the grouped colwise casts (per-group padded scales)
+    # (uneven groups whose token counts are multiples of 128, as padded
+    # mixture-of-experts token groups are: every group's tokens start on a
+    # 128-byte boundary of the operand rows)
     x = synth.normal_bf16((gm, gk), 1.0, seed=76, device=inp.gate.device)
-    _, qa, _, sa = mx.mxfp8_quant_2d_grouped(dy, offs, stream=stream)
-    _, qb, _, sb = mx.mxfp8_quant_2d_grouped(x, offs, stream=stream)
+    ends = torch.tensor([3072, 7168, 11776, 16640], dtype=torch.int32, device=inp.gate.device)
+    _, qa, _, sa = mx.mxfp8_quant_2d_grouped(dy, ends, stream=stream)
+    _, qb, _, sb = mx.mxfp8_quant_2d_grouped(x, ends, stream=stream)
     del dy, x
     cw = torch.empty((ng, gn, gk), dtype=torch.float32, device=inp.gate.device)
-    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm_k(qa, sa, qb, sb, offs, out=cw, stream=stream), 20, 10)
+    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm_k(qa, sa, qb, sb, ends, out=cw, stream=stream), 20, 10)
     tflops = 2.0 * gm * gn * gk / avg / 1e12
     res["wgrad_grouped_gemm_k_8192x5120_t16640_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
                                                        "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
-    del qa, sa, qb, sb, cw, offs
+    del qa, sa, qb, sb, cw, offs, ends
     torch.cuda.empty_cache()
     # the grouped casts at 131072 x 8192 (8 token groups): colwise scales in
     # the per-group padded layout, the same bytes as the plain casts

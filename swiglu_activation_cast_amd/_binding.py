@@ -124,14 +124,18 @@ def _layout(rowwise: bool, colwise: bool) -> int:
 def alloc_outputs(M: int, W: int, layout: int, device, n_groups: int = 0) -> Tuple[torch.Tensor, ...]:
     """Empty (q_row, q_col, s_row, s_col) for an [M, W] result.  With token
     groups (n_groups > 0) s_col is [W, M/32 + 16 n_groups], the per-group
-    padded layout (positions no block maps to are zero)."""
+    padded layout (positions no block maps to are zero), in rows whose
+    stride is rounded up to 16 bytes, so that the grouped GEMMs read every
+    group's scales 16 bytes at a time."""
     empty = torch.empty(0, dtype=torch.uint8, device=device)
     q_row = torch.empty((M, W), dtype=torch.uint8, device=device) if layout & ROWWISE else empty
     s_row = torch.empty((M, W // 32), dtype=torch.uint8, device=device) if layout & ROWWISE else empty
     q_col = torch.empty((W, M), dtype=torch.uint8, device=device) if layout & COLWISE else empty
-    if layout & COLWISE:
-        s_col = (torch.zeros if n_groups else torch.empty)((W, M // 32 + 16 * n_groups), dtype=torch.uint8,
-                                                             device=device)
+    if layout & COLWISE and n_groups:
+        width = M // 32 + 16 * n_groups
+        s_col = torch.zeros((W, -(-width // 16) * 16), dtype=torch.uint8, device=device)[:, :width]
+    elif layout & COLWISE:
+        s_col = torch.empty((W, M // 32), dtype=torch.uint8, device=device)
     else:
         s_col = empty
     return q_row, q_col, s_row, s_col

@@ -269,29 +269,45 @@ __device__ __forceinline__ TilePos tile_pos(const Args &a, u32 L) {
 // For a row of blocks starting at tokens t_k = m0 + 32 k (k = 0..3, t_k < M)
 // the wavefront finds g = the first index whose rounded end exceeds t (the
 // ends before it are all <= t, so the clamped end of group g - 1 is their
-// maximum, which is s).  Lanes read 64 ends at a time; a ballot finds the
-// first end past t and a max reduction over the lanes before it gives s.
-__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d));
+// running maximum, which is s).  Lanes hold 64 rounded ends at a time: a
+// ballot finds the first end past t, and an inclusive max-scan across the
+// lanes gives the running maximum before it.
+//
+// Rounded end of group j as the lane holding it reads it (ends past the
+// list read as "past every token").
+__device__ __forceinline__ int32_t rounded_end(const int32_t *grp, int32_t n, int32_t j) {
+  const int32_t e = *gptr(grp + min(j, n - 1));  // in bounds for every lane
+  return j >= n ? INT32_MAX : (e <= 0 ? 0 : (e & ~31));
+}
+
+// Inclusive running max over the lanes of a wavefront (non-negative values):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then the last lane of
+// each row is folded into the rows after it.
+__device__ __forceinline__ int32_t wave_scan_max(int32_t v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false));  // row_bcast:15 -> rows 1, 3
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false));  // row_bcast:31 -> rows 2, 3
   return v;
 }
 
-__device__ __forceinline__ void group_block_pos(const int32_t *grp, int32_t n, int64_t m0, u32 pos[4]) {
+// r0: this lane's rounded end of group `lane` (the first 64 groups), loaded
+// early by the caller; later groups are read here.
+__device__ __forceinline__ void group_block_pos(const int32_t *grp, int32_t n, int32_t r0, int64_t m0, u32 pos[4]) {
   const int lane = threadIdx.x & 63;
   int32_t g[4] = {-1, -1, -1, -1}, s[4] = {0, 0, 0, 0};
   for (int32_t j0 = 0; j0 < n; j0 += 64) {  // uniform
-    const int32_t j = j0 + lane;
-    const int32_t ej = *gptr(grp + min(j, n - 1));  // in bounds for every lane
-    const int32_t e = j < n ? ej : INT32_MAX;
-    const int32_t r = e <= 0 ? 0 : (e & ~31);  // ends past the list read as "past every token"
+    const int32_t r = j0 == 0 ? r0 : rounded_end(grp, n, j0 + lane);
+    const int32_t scan = wave_scan_max(r < INT32_MAX ? r : 0);  // running max of real ends
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       if (g[k] >= 0) continue;  // uniform
       const int32_t t = (int32_t)m0 + 32 * k;
       const unsigned long long past = __ballot(r > t);
       const int first = past ? __builtin_ctzll(past) : 64;
-      s[k] = max(s[k], wave_max_i32(lane < first ? r : 0));
+      if (first > 0) s[k] = max(s[k], __builtin_amdgcn_readlane(scan, first - 1));
       if (past) g[k] = j0 + first;
     }
   }
@@ -308,8 +324,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
   __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
   const TilePos T = tile_pos(a, xcd_remap(blockIdx.x, gridDim.x));
   const int t = threadIdx.x;
-  u32 gpos[4] = {0, 0, 0, 0};  // padded positions of the tile's four row blocks (token groups)
-  if constexpr (GROUPS) group_block_pos(a.grp, a.n_grp, T.m0, gpos);
 
   // ---- load + compute: thread owns rows m0 + kRPT*rg + i, columns col..col+7
   const int cc = t % kCPR, rg = t / kCPR;
@@ -321,6 +335,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
   // stay in bounds, and their values only reach 32-row blocks or a lane's
   // own columns that are never stored (M is a multiple of 32 here).
   const u32 rmax = (u32)min<int64_t>(a.M - 1 - T.m0, kTM - 1);
+  int32_t r_grp0 = 0;
   {
     V4 in[kRPT][Op::IN];
 #pragma unroll
@@ -332,9 +347,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
         in[i][j] = load16_stream(byte_off(tp, (r * (u32)a.ld_in[j] + cl) * 2u));
       }
     }
+    // token groups: the first 64 group ends, loaded behind the tile's inputs
+    if constexpr (GROUPS) r_grp0 = rounded_end(a.grp, a.n_grp, t & 63);
 #pragma unroll
     for (int i = 0; i < kRPT; i++) Op::apply(in[i], out[i]);
   }
+  u32 gpos[4] = {0, 0, 0, 0};  // padded positions of the tile's four row blocks (token groups)
+  if constexpr (GROUPS) group_block_pos(a.grp, a.n_grp, r_grp0, T.m0, gpos);
 
   if constexpr (ROWS) {
 #pragma unroll
