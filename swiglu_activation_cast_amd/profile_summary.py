@@ -47,6 +47,7 @@ class Call:
     read: int  # algorithmic bytes per launch
     write: int
     grid: int  # workgroups
+    flops: int = 0  # matrix-core work per launch (the GEMM consumer), reported as TFLOP/s
 
 
 def _tiles(M, N, E=1):
@@ -97,7 +98,8 @@ def bench_calls(workload: str, experts: int):
         tiles_m = -(-gm // 256) + (G if mode == 1 else 0)
         grid = tiles_m * -(-gn // 256) * (G if mode == 2 else 1)
         rd = gm * gk + gn * gk * (G if mode == 1 else 1)
-        calls.append(Call(f"k_mx_gemm<{mode}>", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid))
+        calls.append(Call(f"k_mx_gemm<{mode}>", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid,
+                          2 * gm * gn * gk))
     gib = COPY_BYTES
     for mix, (nr, nw) in (("4:1", (4, 1)), ("2:1", (2, 1)), ("3:1", (3, 1)), ("3:2", (3, 2)), ("1:1", (1, 1))):
         for u, grid in STREAM_CONFIGS:
@@ -214,7 +216,8 @@ def stats(csv_path, workload, experts, command, out, top_other=6):
         *[f"# command: {c}" for c in command],
         f"# kernel source hash (bench.py kernel_source_hash): {_build.kernel_source_hash()}",
         "# columns: call, kernel, grid (workgroups), dispatches, avg / median / min / max us,",
-        "#          algorithmic GB/s at the average, % of 8 TB/s",
+        "#          algorithmic GB/s at the average and % of 8 TB/s (the GEMM consumer: TFLOP/s and %",
+        "#          of the 5.0 PFLOP/s dense fp8 peak)",
         "",
     ]
     other = []
@@ -225,13 +228,15 @@ def stats(csv_path, workload, experts, command, out, top_other=6):
             other.append((sum(d), kernel, grid, d))
             continue
         avg = sum(d) / len(d)
-        gbps = metrics.gbps(c.read + c.write, avg * 1e-6)
+        if c.flops:
+            rate, peak, unit = c.flops / (avg * 1e-6) / 1e12, metrics.MFMA_FP8_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            rate, peak, unit = metrics.gbps(c.read + c.write, avg * 1e-6), metrics.HBM_PEAK_GBPS, "GB/s"
         labelled.append((c.label, _short(kernel), grid // THREADS, len(d), avg, statistics.median(d), min(d), max(d),
-                         gbps))
+                         rate, 100 * rate / peak, unit))
     order = {c.label: i for i, c in enumerate(calls)}
     for row in sorted(labelled, key=lambda r: order[r[0]]):
-        lines.append("%-24s %-34s %7d %4d %9.1f %9.1f %9.1f %9.1f %8.1f %6.2f%%" % (
-            *row, 100 * row[-1] / metrics.HBM_PEAK_GBPS))
+        lines.append("%-24s %-34s %7d %4d %9.1f %9.1f %9.1f %9.1f %8.1f %6.2f%% %s" % row)
     if other:
         lines += ["", "# other kernels (not a bench call), by total time: dispatches, avg us, kernel"]
         for tot, kernel, grid, d in sorted(other, reverse=True)[:top_other]:
@@ -273,6 +278,21 @@ def counters(dirs, pattern, command, out, simds=1024, xcds=8, grid=None):
     if "TCC_HIT_sum" in mean and "TCC_MISS_sum" in mean:
         hit = mean["TCC_HIT_sum"] / (mean["TCC_HIT_sum"] + mean["TCC_MISS_sum"])
         derived.append(f"L2 hit rate: {100 * hit:.1f}%")
+    if "TCC_EA0_WRREQ_sum" in mean and "TCC_EA0_WRREQ_64B_sum" in mean:
+        n, n64 = mean["TCC_EA0_WRREQ_sum"], mean["TCC_EA0_WRREQ_64B_sum"]
+        derived.append(f"L2->memory writes: {n64:.4g} 64-byte and {n - n64:.4g} 32-byte requests, "
+                       f"{(64 * n64 + 32 * (n - n64)) / 1e9:.4f} GB")
+    if "TCC_EA0_RDREQ_sum" in mean:
+        derived.append(f"L2->memory reads: {mean['TCC_EA0_RDREQ_sum']:.4g} requests")
+    cycles = mean.get("GRBM_GUI_ACTIVE", 0.0) / xcds  # per XCD (the counter is summed over XCDs)
+    if cycles:
+        derived.append(f"active cycles per XCD: {cycles:.4g}")
+        for c, what in (("TCC_EA0_RDREQ_LEVEL_sum", "read"), ("TCC_EA0_WRREQ_LEVEL_sum", "write")):
+            if c in mean:
+                derived.append(f"L2->memory {what} requests in flight (mean over active cycles): {mean[c] / cycles:.0f}")
+        if "SQ_ACTIVE_INST_VALU" in mean:
+            derived.append(f"VALUBusy (rocprof's formula, SQ_ACTIVE_INST_VALU / CUs / active cycles): "
+                           f"{100 * mean['SQ_ACTIVE_INST_VALU'] / (simds // 4) / cycles:.1f}%")
     if derived:
         lines += ["", *[f"# {x}" for x in derived]]
     with open(out, "w") as f:

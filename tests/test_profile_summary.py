@@ -104,7 +104,7 @@ def test_stats_per_call(tmp_path):
     assert float(lines["quant2d_col"][4]) == pytest.approx(510.0)
     assert float(lines["quant3d_E64"][4]) == pytest.approx(1410.0)
     gbps = (c["quant3d_E64"].read + c["quant3d_E64"].write) / 1410e-6 / 1e9
-    assert float(lines["quant3d_E64"][8]) == pytest.approx(gbps, abs=0.1)
+    assert float(lines["quant3d_E64"][8]) == pytest.approx(gbps, abs=0.1) and lines["quant3d_E64"][10] == "GB/s"
     assert "other kernels" in out.read_text()
 
 
