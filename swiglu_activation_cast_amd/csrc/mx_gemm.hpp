@@ -21,11 +21,13 @@
 // 8 (v / 4) + 4 (l / 32) + v % 4, column l % 32.
 //
 // Structure: a 256 x 256 C tile per 256-thread workgroup, one workgroup per
-// CU (148 KB of LDS); each wavefront owns 128 x 128 of C, its 256
-// accumulators in AGPRs.  K is staged 128 at a time (two MFMA steps) in a
-// double-buffered LDS ring filled by direct global -> LDS loads; each stage
-// reads all its operands from LDS, then issues the next stage's loads, then
-// its 32 MFMAs, so the loads run under the matrix work.
+// CU; each wavefront owns 128 x 128 of C, its 256 accumulators in AGPRs.  K
+// is staged 64 at a time (one MFMA step) in a ring of four LDS slots filled
+// by direct global -> LDS loads issued three stages ahead.  While a stage's
+// 16 MFMAs run from registers, the wavefront reads the next stage's operands
+// from LDS into a second register set and issues the loads of the stage
+// three ahead, one instruction between consecutive MFMAs, so that the
+// matrix cores, the LDS and the vector memory unit work at once.
 #pragma once
 #include "mx_kernels.hpp"
 
@@ -58,38 +60,67 @@ enum GemmMode { kGemmPlain = 0, kGemmGroupM = 1, kGemmGroupK = 2 };
 
 constexpr int kMaxGroups = 1024;
 
-// 16 zero bytes in device memory: the source of operand chunks at or past K
-__device__ __attribute__((aligned(16))) const uint8_t kZeroChunk[16] = {};
-
 typedef int v8i_t __attribute__((ext_vector_type(8)));
 typedef float v16f_t __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256, kBN = 256;  // C tile per workgroup
-constexpr int kBK = 128;              // K per LDS stage: two MFMA steps, whole 128-byte lines
+constexpr int kBK = 64;               // K per stage: one MFMA step
+constexpr int kRing = 4;              // LDS stage slots
+constexpr int kAhead = 3;             // stages whose loads are issued ahead of the one computed
 constexpr int kGroup = 4;             // tile rows per group in the tile order
 constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 128 of C
-constexpr int kStageA = kBM * kBK, kStageB = kBN * kBK;  // one stage of each operand in LDS (bytes)
-constexpr int kSG = 16;                                  // scale blocks per LDS scale group
+constexpr int kSlot = kBM * kBK;      // bytes of one operand in one slot (16 KB)
+constexpr int kLoadsPerStage = 8;     // direct loads per wavefront and stage: 4 of A, 4 of B
+constexpr int kSG = 16;               // scale blocks per LDS scale group
 constexpr int kStagesPerGroup = kSG / (kBK / 32);
-static_assert(kStagesPerGroup >= 2, "a scale group is written to LDS in its second stage");
+static_assert(kBM == kBN, "the operand load layout assumes square tiles");
 
-__device__ __forceinline__ u32x4_t gload16(const uint8_t *p) {
-  return *gptr(reinterpret_cast<const u32x4_t *>(p));
+// LDS position of 16-byte chunk kc (0..3) of tile row `row`: rows of 64
+// bytes, chunks XOR-permuted by (row / 4) % 4, so that the 16 lanes of one
+// quarter-wave reading the same chunk of 16 consecutive rows hit 16
+// different 16-byte bank groups.
+__device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * (u32)kBK + ((kc ^ ((row >> 2) & 3u)) << 4); }
+
+__device__ __forceinline__ u32 lds_addr(const void *p) {
+  return (u32)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
-// LDS position of 16-byte chunk kc (0..7) of tile row `row`: rows of 128
-// bytes, chunks XOR-permuted by (row / 2) % 8, so that the 16 lanes of one
-// quarter-wave reading the same chunk of 16 consecutive rows hit 16
-// different 4-bank groups.
-__device__ __forceinline__ u32 lds_off(u32 row, u32 kc) { return row * kBK + ((kc ^ ((row >> 1) & 7u)) << 4); }
+// Direct global -> LDS load: lane l's 16 bytes at base + off land at LDS
+// byte `lds` + 16 l (global_load_lds_dwordx4, saddr form).  Written as asm so
+// that the compiler does not wait for it before LDS reads of other slots;
+// its completion is awaited with wait_vm.  M0 holds the LDS base: it is
+// saved and restored, and an SALU write of M0 needs one wait state before
+// an LDS DMA reads it.
+__device__ __forceinline__ void load_lds(const uint8_t *base, u32 off, u32 lds) {
+  u32 saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_nop 0\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(off), "s"(base));
+}
+// Wait until at most N of this wavefront's vector memory operations are in
+// flight (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
-template <int MODE>
+// NT: C written with nontemporal stores (K-long tiles: the stores then do
+// not displace operand lines from L2); otherwise ordinary stores, faster
+// when the tile is short in K.
+template <int MODE, bool NT>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t smemA[2][kStageA], smemB[2][kStageB];  // [buffer]
+  __shared__ __attribute__((aligned(1024))) uint8_t smA[kRing][kSlot], smB[kRing][kSlot];  // [slot]
   // scale table of one group of kSG blocks: row q < kBM is A's tile row q,
   // row kBM + q is B's tile row q  [buffer][row][block]
-  __shared__ __attribute__((aligned(16))) uint8_t smemS[2][kBM + kBN][kSG];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  __shared__ __attribute__((aligned(1024))) uint8_t smS[2][kBM + kBN][kSG];
+  const int t = threadIdx.x, lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
 
   // Tile order: each XCD takes one contiguous range of tiles; inside it,
@@ -136,7 +167,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
       before += nt;
       start = end;
     }
-    if (e_hit < 0) return;  // uniform over the workgroup: past the real tiles
+    // the walk is uniform; make that visible to the compiler, so that the
+    // tile's bases live in scalar registers
+    e_hit = __builtin_amdgcn_readfirstlane(e_hit);
+    if (e_hit < 0) return;  // past the real tiles
+    m_base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((u32)((uint64_t)m_base >> 32)) << 32) |
+                       __builtin_amdgcn_readfirstlane((u32)m_base));
+    m_end = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((u32)((uint64_t)m_end >> 32)) << 32) |
+                      __builtin_amdgcn_readfirstlane((u32)m_end));
     b_mat = g.b + (int64_t)e_hit * g.stride_b;
     sb_mat = g.sb + (int64_t)e_hit * g.stride_sb;
   }
@@ -148,9 +186,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     int64_t start = 0, end = 0;
     for (int64_t e = 0; e <= kgrp; e++) {  // uniform
       const int32_t v = g.offs[e];
-      const int64_t r = v <= 0 ? 0 : (int64_t)(v & ~31);
+      const int64_t rr = v <= 0 ? 0 : (int64_t)(v & ~31);
       start = end;
-      end = min<int64_t>(max<int64_t>(r, start), g.K);
+      end = min<int64_t>(max<int64_t>(rr, start), g.K);
     }
     k_lo = start;
     Kt = end - start;
@@ -161,25 +199,77 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   // Rows past M (N) are read as the last row: in bounds, never stored.
   const uint8_t *a_tile = g.a + m_base * g.lda + k_lo, *b_tile = b_mat + n_base * g.ldb + k_lo;  // uniform
   const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
-
-  // ---- scales: moved to LDS kSG blocks (kStagesPerGroup stages) at a
-  // time, thread t taking A's and B's tile row t.  Blocks past K / 32 read
-  // as 127 (2^0) against zero data.  One byte load per lane per operand
-  // tile and stage, from 32 rows at once, is far slower than this.
   const uint8_t *sa_tile = g.sa + m_base * g.ld_sa + s_lo, *sb_tile = sb_mat + n_base * g.ld_sb + s_lo;  // uniform
   const int64_t nblk = Kt / 32;
   const int nstage = (int)((Kt + kBK - 1) / kBK);
   const int ngroup = (int)((nblk + kSG - 1) / kSG);
-  const u32 sa_row = min((u32)t, a_rows - 1), sb_row = min((u32)t, b_rows - 1);
 
-  u32x4_t ssa, ssb;  // the next scale group, global -> registers -> LDS
-  auto load_scales = [&](int grp) {
-    const int64_t b0 = (int64_t)grp * kSG;
-    if (g.scale_vec && b0 + kSG <= nblk) {  // uniform
-      ssa = gload16(byte_off(sa_tile + b0, sa_row * (u32)g.ld_sa));
-      ssb = gload16(byte_off(sb_tile + b0, sb_row * (u32)g.ld_sb));
+  // ---- operand loads.  Slab p = 4 w + q (q = 0..3) of a slot holds tile
+  // rows 16 p .. 16 p + 15; lane l loads row 16 p + l / 4 into stored chunk
+  // l % 4, which holds logical chunk (l % 4) ^ the row's key; the key
+  // (row / 4) % 4 = (l / 16) % 4 is the same for every slab.
+  const u32 kc16 = (((u32)lane & 3u) ^ (((u32)lane >> 4) & 3u)) * 16u;
+  u32 a_roff[4], b_roff[4];
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const u32 row = 16u * (4u * (u32)w + (u32)q) + ((u32)lane >> 2);
+    a_roff[q] = min(row, a_rows - 1) * (u32)g.lda;
+    b_roff[q] = min(row, b_rows - 1) * (u32)g.ldb;
+  }
+  // Stage st goes to slot st % kRing.  Loads of stages past the last re-read
+  // the last one into a free slot (never read); chunks at or past K read
+  // chunk 0 of their row and are zeroed in LDS before the stage is read.
+  auto stage_base = [&](int st_, const uint8_t *&ba, const uint8_t *&bb, u32 &kc) {
+    const int64_t k0 = (int64_t)min(st_, nstage - 1) * kBK;
+    ba = a_tile + k0;
+    bb = b_tile + k0;
+    kc = (int64_t)kc16 < Kt - k0 ? kc16 : 0u;
+  };
+  auto load_stage = [&](int st_) {
+    const uint8_t *ba, *bb;
+    u32 kc;
+    stage_base(st_, ba, bb, kc);
+    const int slot = st_ & (kRing - 1);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const u32 p = 4u * (u32)w + (u32)q;
+      load_lds(ba, a_roff[q] + kc, lds_addr(&smA[slot][p * 1024u]));
+      load_lds(bb, b_roff[q] + kc, lds_addr(&smB[slot][p * 1024u]));
+    }
+  };
+  auto zero_tail = [&](int st_) {  // this thread's chunks of stage st_ at or past K -> 0
+    const int64_t kmax = Kt - (int64_t)st_ * kBK;
+    const int slot = st_ & (kRing - 1);
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const u32 p = 4u * (u32)w + (u32)q;
+      if ((int64_t)kc16 >= kmax) {
+        *reinterpret_cast<u32x4_t *>(&smA[slot][p * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
+        *reinterpret_cast<u32x4_t *>(&smB[slot][p * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
+      }
+    }
+  };
+
+  // ---- scales, kSG blocks (kStagesPerGroup stages) at a time, into buffer
+  // group % 2.  Full groups of 16-byte-aligned scale rows go global -> LDS
+  // directly: wavefront w fills table rows 128 w .. 128 w + 127, lane l one
+  // row.  Otherwise thread t reads A's and B's tile row t byte by byte,
+  // blocks past K / 32 reading 127 (2^0) against zero data.
+  auto group_vec = [&](int gi) { return g.scale_vec && (int64_t)(gi + 1) * kSG <= nblk; };
+  const u32 sa_row = min((u32)t, a_rows - 1), sb_row = min((u32)t, b_rows - 1);
+  auto load_scales = [&](int gi) {
+    const int64_t b0 = (int64_t)gi * kSG;
+    if (group_vec(gi)) {
+#pragma unroll
+      for (int q = 0; q < 2; q++) {
+        const u32 trow0 = 64u * (2u * (u32)w + (u32)q);  // uniform: 64 rows of one operand
+        const u32 trow = trow0 + (u32)lane;
+        const bool is_a = trow0 < (u32)kBM;
+        const uint8_t *base = is_a ? sa_tile + b0 : sb_tile + b0;
+        const u32 off = is_a ? min(trow, a_rows - 1) * (u32)g.ld_sa : min(trow - kBM, b_rows - 1) * (u32)g.ld_sb;
+        load_lds(base, off, lds_addr(&smS[gi & 1][trow0][0]));
+      }
     } else {
-      // byte by byte, from clamped (in-bounds) positions; blocks past K / 32 read as 127
       u32 wa[4] = {0, 0, 0, 0}, wb[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < kSG; j++) {
@@ -190,55 +280,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
         wa[j / 4] |= (ok ? va : 127u) << (8 * (j % 4));
         wb[j / 4] |= (ok ? vb : 127u) << (8 * (j % 4));
       }
-      ssa = u32x4_t{wa[0], wa[1], wa[2], wa[3]};
-      ssb = u32x4_t{wb[0], wb[1], wb[2], wb[3]};
+      *reinterpret_cast<u32x4_t *>(&smS[gi & 1][t][0]) = u32x4_t{wa[0], wa[1], wa[2], wa[3]};
+      *reinterpret_cast<u32x4_t *>(&smS[gi & 1][kBM + t][0]) = u32x4_t{wb[0], wb[1], wb[2], wb[3]};
     }
   };
-  // Table row q keeps its 4 dwords rotated by (q / 16) % 4, so that 32
-  // consecutive rows read at one dword position hit 32 different banks.
-  auto rot = [](u32x4_t v, u32 k) {  // dword j moves to position (j + k) % 4
-    const u32 w0 = k == 0 ? v.x : k == 1 ? v.w : k == 2 ? v.z : v.y;
-    const u32 w1 = k == 0 ? v.y : k == 1 ? v.x : k == 2 ? v.w : v.z;
-    const u32 w2 = k == 0 ? v.z : k == 1 ? v.y : k == 2 ? v.x : v.w;
-    const u32 w3 = k == 0 ? v.w : k == 1 ? v.z : k == 2 ? v.y : v.x;
-    return u32x4_t{w0, w1, w2, w3};
+
+  // One stage's operands and scales in registers.  Lane r + 32 h takes, for
+  // each 32-row tile, chunks h and 2 + h of its row (block h of the step:
+  // elements 16 h .. 16 h + 15 of each of the step's two 32-element
+  // halves), and the scale byte of block 2 (stage % 8) + h of its row,
+  // shifted to byte 0 (op_sel 0).
+  struct Ops {
+    v8i_t a[4], b[4];
+    int sa[4], sb[4];
   };
-  auto store_scales = [&](int buf) {
-    const u32 k = ((u32)t >> 4) & 3u;  // kBM is a multiple of 64: the same key for both halves
-    *reinterpret_cast<u32x4_t *>(&smemS[buf][t][0]) = rot(ssa, k);
-    *reinterpret_cast<u32x4_t *>(&smemS[buf][kBM + t][0]) = rot(ssb, k);
-  };
-  // this stage's 4 scale bytes of table row q, shifted so that the block of
-  // step s for this lane's half (block 2 s + h) is byte 2 s (op_sel 2 s)
-  auto read_scales = [&](int buf, u32 q, int in_grp_) {
-    const u32 pos = ((u32)in_grp_ + (q >> 4)) & 3u;
-    const u32 v = *reinterpret_cast<const u32 *>(&smemS[buf][q][4u * pos]);
-    return (int)(v >> (8u * (u32)h));
-  };
-  // ---- operands: global -> LDS directly (global_load_lds_dwordx4: lane
-  // l's 16 bytes land at the instruction's LDS base + 16 l).  Wave w fills
-  // 1 KB slabs p = 8 w + q (q = 0..7) of each operand's stage buffer, i.e.
-  // tile rows 8 p .. 8 p + 7; lane l writes slab bytes 16 l .. 16 l + 15,
-  // which hold row 8 p + l / 8, stored chunk l % 8, i.e. logical chunk
-  // (l % 8) ^ the row's XOR key.  Chunks at or past K, and so every chunk
-  // of a stage past the last, are read from kZeroChunk.
-  auto dma_stage = [&](int st_, int buf_) {
-    const int64_t k0 = (int64_t)st_ * kBK;
+  auto read_stage = [&](int st_, Ops &o) {
+    const int slot = st_ & (kRing - 1), gi = st_ / kStagesPerGroup, in_g = st_ % kStagesPerGroup;
+    const u32 sh = 8u * (u32)h + 16u * (u32)(in_g & 1);
 #pragma unroll
-    for (int q = 0; q < 8; q++) {
-      const u32 p = (u32)w * 8u + (u32)q;
-      const u32 row = 8u * p + ((u32)lane >> 3), kc = ((u32)lane & 7u) ^ ((row >> 1) & 7u);
-      const bool in_k = k0 + 16 * (int64_t)kc < Kt;
-      const u32 ra = min(row, a_rows - 1), rb = min(row, b_rows - 1);
-      const uint8_t *pa = in_k ? byte_off(a_tile + k0, ra * (u32)g.lda + kc * 16u) : kZeroChunk;
-      const uint8_t *pb = in_k ? byte_off(b_tile + k0, rb * (u32)g.ldb + kc * 16u) : kZeroChunk;
-      __builtin_amdgcn_global_load_lds((const MX_GLOBAL void *)gptr(pa),
-                                       (__attribute__((address_space(3))) void *)&smemA[buf_][p * 1024u], 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const MX_GLOBAL void *)gptr(pb),
-                                       (__attribute__((address_space(3))) void *)&smemB[buf_][p * 1024u], 16, 0, 0);
+    for (int x = 0; x < 4; x++) {
+      const u32 ra = (u32)(wm * 128 + 32 * x + r), rb = (u32)(wn * 128 + 32 * x + r);
+      const u32x4_t la = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, (u32)h)]);
+      const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, 2u + (u32)h)]);
+      const u32x4_t lb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, (u32)h)]);
+      const u32x4_t hb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, 2u + (u32)h)]);
+      o.a[x] = v8i_t{(int)la.x, (int)la.y, (int)la.z, (int)la.w, (int)ha.x, (int)ha.y, (int)ha.z, (int)ha.w};
+      o.b[x] = v8i_t{(int)lb.x, (int)lb.y, (int)lb.z, (int)lb.w, (int)hb.x, (int)hb.y, (int)hb.z, (int)hb.w};
+      o.sa[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][ra][4 * (in_g / 2)]) >> sh);
+      o.sb[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][kBM + rb][4 * (in_g / 2)]) >> sh);
     }
   };
-  constexpr int kWaitVm0 = 0x0F70;  // s_waitcnt vmcnt(0), other counters not waited
 
   v16f_t acc[4][4];
 #pragma unroll
@@ -246,83 +317,149 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; j++) acc[i][j] = v16f_t{};
 
-  if (nstage > 0) dma_stage(0, 0);
-  if (ngroup > 0) load_scales(0);  // K = 0: no scale is read
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  if (ngroup > 0) store_scales(0);
-  __syncthreads();
-
-  for (int st = 0; st < nstage; st++) {
-    const int buf = st & 1;
-    const int grp = st / kStagesPerGroup, in_grp = st % kStagesPerGroup;
-    const bool more_scales = grp + 1 < ngroup;  // uniform
-    // the next scale group: fetched in the group's first stage, written to
-    // LDS at the start of its second (the fetch completed with the first
-    // stage's data), into the buffer whose last reads ended with the
-    // previous group; first read after a later barrier
-    if (more_scales && in_grp == 1) store_scales((grp + 1) & 1);
-    if (more_scales && in_grp == 0) load_scales(grp + 1);
-    // this stage's operands and scales for both MFMA steps, all read before
-    // the first MFMA in the order the MFMAs consume them; in step s lane
-    // r + 32 h takes block 4 in_grp + 2 s + h of its row in each 32-row
-    // tile, byte 2 s of the scale word (op_sel 2 s)
-    int csa[4], csb[4];
-    v8i_t av[2][4], bv[2][4];
-    auto read_op = [&](const uint8_t *base, u32 row, u32 s) {
-      const u32x4_t lo = *reinterpret_cast<const u32x4_t *>(&base[lds_off(row, 4u * s + h)]);
-      const u32x4_t hi = *reinterpret_cast<const u32x4_t *>(&base[lds_off(row, 4u * s + 2u + h)]);
-      return v8i_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-    };
+  // One stage: the MFMAs of stage st from `cur`; between them, the loads of
+  // stage st + kAhead (its slot held stage st - 1, whose reads ended before
+  // the previous barrier) and the reads of stage st + 1 into `nxt` (read
+  // unconditionally: past the last stage the slot holds data never used).
+  // Then wait until stage st + 2 has landed and meet the barrier.  st = -1
+  // is a leading all-zero stage that makes the stage count even.
+  auto body = [&](int st, Ops &cur, Ops &nxt) {
+    if (st >= 0 && st % kStagesPerGroup == 0 && st / kStagesPerGroup + 1 < ngroup)
+      load_scales(st / kStagesPerGroup + 1);  // its buffer was last read by the previous group
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t *ba, *bb;
+    u32 kc;
+    stage_base(st + kAhead, ba, bb, kc);
+    const int lslot = (st + kAhead) & (kRing - 1);
+    const int rs = st + 1, rslot = rs & (kRing - 1), rgi = rs / kStagesPerGroup, rin = rs % kStagesPerGroup;
+    u32x4_t la[4], ha[4], lb[4], hb[4];
+    u32 wsa[4], wsb[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++) csa[i] = read_scales(grp & 1, (u32)(wm * 128 + 32 * i + r), in_grp);
+    for (int k = 0; k < 16; k++) {
+      const int i = k / 4, j = k % 4;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0, cur.sa[i], 0,
+                                                                   cur.sb[j]);
+      if (k < 8) {
+        const int q = k / 2;
+        const u32 p = 4u * (u32)w + (u32)q;
+        if (k % 2 == 0) load_lds(ba, a_roff[q] + kc, lds_addr(&smA[lslot][p * 1024u]));
+        else load_lds(bb, b_roff[q] + kc, lds_addr(&smB[lslot][p * 1024u]));
+      }
+      const int x = k / 4, part = k % 4;
+      const u32 ra = (u32)(wm * 128 + 32 * x + r), rb = (u32)(wn * 128 + 32 * x + r);
+      if (part == 0) {
+        la[x] = *reinterpret_cast<const u32x4_t *>(&smA[rslot][lds_off(ra, (u32)h)]);
+        wsa[x] = *reinterpret_cast<const u32 *>(&smS[rgi & 1][ra][4 * (rin / 2)]);
+      }
+      if (part == 1) ha[x] = *reinterpret_cast<const u32x4_t *>(&smA[rslot][lds_off(ra, 2u + (u32)h)]);
+      if (part == 2) {
+        lb[x] = *reinterpret_cast<const u32x4_t *>(&smB[rslot][lds_off(rb, (u32)h)]);
+        wsb[x] = *reinterpret_cast<const u32 *>(&smS[rgi & 1][kBM + rb][4 * (rin / 2)]);
+      }
+      if (part == 3) hb[x] = *reinterpret_cast<const u32x4_t *>(&smB[rslot][lds_off(rb, 2u + (u32)h)]);
+      __builtin_amdgcn_sched_barrier(0);  // keep this order: one load or read between MFMAs
+    }
+    const u32 sh = 8u * (u32)h + 16u * (u32)(rin & 1);
 #pragma unroll
-    for (int j = 0; j < 4; j++) csb[j] = read_scales(grp & 1, (u32)(kBM + wn * 128 + 32 * j + r), in_grp);
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-      av[s][0] = read_op(smemA[buf], (u32)(wm * 128 + r), s);
-#pragma unroll
-      for (int j = 0; j < 4; j++) bv[s][j] = read_op(smemB[buf], (u32)(wn * 128 + 32 * j + r), s);
-#pragma unroll
-      for (int i = 1; i < 4; i++) av[s][i] = read_op(smemA[buf], (u32)(wm * 128 + 32 * i + r), s);
+    for (int x = 0; x < 4; x++) {
+      nxt.a[x] = v8i_t{(int)la[x].x, (int)la[x].y, (int)la[x].z, (int)la[x].w,
+                       (int)ha[x].x, (int)ha[x].y, (int)ha[x].z, (int)ha[x].w};
+      nxt.b[x] = v8i_t{(int)lb[x].x, (int)lb[x].y, (int)lb[x].z, (int)lb[x].w,
+                       (int)hb[x].x, (int)hb[x].y, (int)hb[x].z, (int)hb[x].w};
+      nxt.sa[x] = (int)(wsa[x] >> sh);
+      nxt.sb[x] = (int)(wsb[x] >> sh);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // The next stage's loads, into the other buffer (its last reads ended at
-    // the previous barrier), issued after every LDS read of this stage: the
-    // compiler waits for such loads before any later LDS read.  Not behind
-    // a branch, so that the MFMAs cannot sink past the scheduling barriers
-    // into a later block (after the last stage it loads zeros into the idle
-    // buffer).
-    dma_stage(st + 1, buf ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
+#if __HIP_DEVICE_COMPILE__
+    // Uses of this stage's results here keep its MFMAs and reads in this
+    // block: the branches below would otherwise let the compiler sink them
+    // past the barrier, where nothing overlaps them.
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int x = 0; x < 4; x++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[0][i], bv[0][j], acc[i][j], 0, 0, 0, csa[i], 0,
-                                                                     csb[j]);
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av[1][i], bv[1][j], acc[i][j], 0, 0, 2, csa[i], 2,
-                                                                     csb[j]);
-    __builtin_amdgcn_sched_barrier(0);
-    // this wave's loads have landed; the barrier makes every wave's visible
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      for (int j = 0; j < 4; j++) asm volatile("" ::"a"(acc[x][j]));
+      asm volatile("" ::"v"(nxt.a[x]), "v"(nxt.b[x]), "v"(nxt.sa[x]), "v"(nxt.sb[x]));
+    }
+#endif
+    wait_vm<kLoadsPerStage>();  // stage st + 2, and scales issued before stage st + kAhead, landed
     __syncthreads();
-  }
+    if ((int64_t)(st + 3) * kBK > Kt && (int64_t)(st + 2) * kBK < Kt) {  // stage st + 2 is the partial last one
+      zero_tail(st + 2);
+      __syncthreads();
+    }
+  };
 
+  Ops o0, o1;
+  const int odd = nstage & 1;
+  if (nstage > 0) {
+    if (ngroup > 0) load_scales(0);
+    load_stage(0);
+    load_stage(1);
+    if (!odd) {
+      load_stage(2);
+      wait_vm<2 * kLoadsPerStage>();  // stage 0 and the scales landed
+    } else {
+      wait_vm<kLoadsPerStage>();
+    }
+    __syncthreads();
+    if ((int64_t)kBK > Kt) {  // stage 0 is partial (then it is the only one)
+      zero_tail(0);
+      __syncthreads();
+    }
+    if (!odd && (int64_t)2 * kBK > Kt) {  // two stages, the second partial
+      wait_vm<kLoadsPerStage>();
+      __syncthreads();
+      zero_tail(1);
+      __syncthreads();
+    }
+    if (!odd) {
+      read_stage(0, o0);
+    } else {  // the leading zero stage
 #pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int64_t col = n_base + wn * 128 + 32 * j + r;
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
-        if (row < m_end && col < g.N) *gptr(c_mat + row * g.ldc + col) = acc[i][j][v];
+      for (int x = 0; x < 4; x++) {
+        o0.a[x] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+        o0.b[x] = v8i_t{0, 0, 0, 0, 0, 0, 0, 0};
+        o0.sa[x] = 127;
+        o0.sb[x] = 127;
       }
     }
+  }
+  for (int st = -odd; st < nstage; st += 2) {
+    body(st, o0, o1);
+    body(st + 1, o1, o0);
+  }
+  wait_vm<0>();  // no load may still be writing this workgroup's LDS when it ends
+
+  // ---- C
+  auto put = [&](float *p, float v) {
+    if constexpr (NT) __builtin_nontemporal_store(v, gptr(p));
+    else *gptr(p) = v;
+  };
+  if (a_rows == (u32)kBM && b_rows == (u32)kBN && g.ldc < (int64_t(1) << 22)) {
+    // whole tile: a uniform row base per (i, v) and a 32-bit lane offset
+    float *c_tile = c_mat + m_base * g.ldc + n_base;
+    const u32 lane_off = ((u32)(wm * 128 + 4 * h) * (u32)g.ldc + (u32)(wn * 128 + r)) * 4u;
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        float *row_base = c_tile + (int64_t)(32 * i + 8 * (v / 4) + (v % 4)) * g.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; j++) put(byte_off(row_base, lane_off + 128u * (u32)j), acc[i][j][v]);
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int64_t col = n_base + wn * 128 + 32 * j + r;
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
+          if (row < m_end && col < g.N) put(c_mat + row * g.ldc + col, acc[i][j][v]);
+        }
+      }
+  }
 }
 
 }  // namespace mx

@@ -496,9 +496,17 @@ mxfp8_status gemm_launch(int mode, const void *a, int64_t lda, const void *sa, i
   g.stride_c = stride_c;
   g.scale_vec = aligned16(sa) && aligned16(sb) && ld_sa % 16 == 0 && ld_sb % 16 == 0 && stride_sb % 16 == 0;
   void *kargs[] = {&g};
-  const void *k = mode == mx::kGemmGroupM   ? (const void *)&mx::k_mx_gemm<mx::kGemmGroupM>
-                  : mode == mx::kGemmGroupK ? (const void *)&mx::k_mx_gemm<mx::kGemmGroupK>
-                                            : (const void *)&mx::k_mx_gemm<mx::kGemmPlain>;
+  // nontemporal C stores for tiles long in K (for the K-grouped form, the
+  // mean group length)
+  const bool nt = (mode == mx::kGemmGroupK ? K / G : K) >= 1024;
+  const void *k = mode == mx::kGemmGroupM
+                      ? (nt ? (const void *)&mx::k_mx_gemm<mx::kGemmGroupM, true>
+                            : (const void *)&mx::k_mx_gemm<mx::kGemmGroupM, false>)
+                  : mode == mx::kGemmGroupK
+                      ? (nt ? (const void *)&mx::k_mx_gemm<mx::kGemmGroupK, true>
+                            : (const void *)&mx::k_mx_gemm<mx::kGemmGroupK, false>)
+                      : (nt ? (const void *)&mx::k_mx_gemm<mx::kGemmPlain, true>
+                            : (const void *)&mx::k_mx_gemm<mx::kGemmPlain, false>);
   hipError_t err = hipLaunchKernel(k, dim3((unsigned)blocks), dim3(mx::kGemmThreads), kargs, 0, (hipStream_t)stream);
   return err == hipSuccess ? MXFP8_OK : MXFP8_ERR_LAUNCH;
 }

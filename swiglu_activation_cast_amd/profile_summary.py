@@ -98,7 +98,7 @@ def bench_calls(workload: str, experts: int):
         tiles_m = -(-gm // 256) + (G if mode == 1 else 0)
         grid = tiles_m * -(-gn // 256) * (G if mode == 2 else 1)
         rd = gm * gk + gn * gk * (G if mode == 1 else 1)
-        calls.append(Call(f"k_mx_gemm<{mode}>", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid,
+        calls.append(Call(f"k_mx_gemm<{mode},", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid,
                           2 * gm * gn * gk))
     gib = COPY_BYTES
     for mix, (nr, nw) in (("4:1", (4, 1)), ("2:1", (2, 1)), ("3:1", (3, 1)), ("3:2", (3, 2)), ("1:1", (1, 1))):

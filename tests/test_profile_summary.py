@@ -113,7 +113,7 @@ def test_counters_mean_and_derived_figures(tmp_path):
     derived matrix-core utilization and L2 hit rate (invented values: 8 XCDs
     of 1000 active cycles each, 1024 SIMDs busy 250 cycles each -> 25 %; 90
     hits, 10 misses -> 90 %)."""
-    k = "void mx::k_mx_gemm<0>(mx::GemmArgs)"
+    k = "void mx::k_mx_gemm<0, true>(mx::GemmArgs)"
     other = "void mx::k_tiled<mx::OpBwd, true, false>(mx::Args)"
     rows = []
     for name, grid, counter, vals in ((k, 2048, "SQ_VALU_MFMA_BUSY_CYCLES", (256000.0, 256000.0)),
@@ -131,7 +131,7 @@ def test_counters_mean_and_derived_figures(tmp_path):
             w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": name, "Grid_Size": grid * 256, "Counter_Name": counter,
                         "Counter_Value": v})
     out = tmp_path / "o.txt"
-    ps.counters([str(d)], "k_mx_gemm<0>", ["cmd"], str(out), grid=2048)
+    ps.counters([str(d)], "k_mx_gemm<0,", ["cmd"], str(out), grid=2048)
     text = out.read_text()
     assert "matrix-core utilization: 25.0%" in text
     assert "L2 hit rate: 90.0%" in text
