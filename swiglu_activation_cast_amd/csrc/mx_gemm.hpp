@@ -26,8 +26,8 @@
 // by direct global -> LDS loads issued three stages ahead.  While a stage's
 // 16 MFMAs run from registers, the wavefront reads the next stage's operands
 // from LDS into a second register set and issues the loads of the stage
-// three ahead, one instruction between consecutive MFMAs, so that the
-// matrix cores, the LDS and the vector memory unit work at once.
+// three ahead (one after every other MFMA), so that the matrix cores, the
+// LDS and the vector memory unit work at once.
 #pragma once
 #include "mx_kernels.hpp"
 
@@ -339,10 +339,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
       const int i = k / 4, j = k % 4;
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0, cur.sa[i], 0,
                                                                    cur.sb[j]);
-      if (k < 8) {
-        const int q = k / 2;
+      if (k % 2 == 0) {  // load k / 2: A's slab q, then B's
+        const int q = k / 4;
         const u32 p = 4u * (u32)w + (u32)q;
-        if (k % 2 == 0) load_lds(ba, a_roff[q] + kc, lds_addr(&smA[lslot][p * 1024u]));
+        if (k % 4 == 0) load_lds(ba, a_roff[q] + kc, lds_addr(&smA[lslot][p * 1024u]));
         else load_lds(bb, b_roff[q] + kc, lds_addr(&smB[lslot][p * 1024u]));
       }
       const int x = k / 4, part = k % 4;
@@ -357,7 +357,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
         wsb[x] = *reinterpret_cast<const u32 *>(&smS[rgi & 1][kBM + rb][4 * (rin / 2)]);
       }
       if (part == 3) hb[x] = *reinterpret_cast<const u32x4_t *>(&smB[rslot][lds_off(rb, 2u + (u32)h)]);
-      __builtin_amdgcn_sched_barrier(0);  // keep this order: one load or read between MFMAs
+      __builtin_amdgcn_sched_barrier(0);  // keep this order: loads and reads spread between the MFMAs
     }
     const u32 sh = 8u * (u32)h + 16u * (u32)(rin & 1);
 #pragma unroll
