@@ -172,11 +172,16 @@ struct ActGelu {
     return g < 0.0f ? q : 1.0f - q;
   }
 
-  // e^(-g^2/2) (g^2 is exact for a bf16 g), times 2^64 when `scaled`
+  // e^(-g^2/2), times 2^64 when `scaled`.  g^2 is exact for a bf16 g (a
+  // normal number unless |g| < 2^-63) and -log2(e)/2 is exactly half of the
+  // float log2(e), so g^2 times it rounds as -(g^2/2) times log2(e) does, in
+  // one multiply fewer; where g^2 is subnormal the two arguments may differ
+  // in the last bit, and the exponential is 1 either way.
+  static constexpr float kNegHalfLog2e = -0.5f * kLog2e;
   template <bool scaled>
   __device__ __forceinline__ static float gauss(float g) {
-    const float h = -0.5f * (g * g);
-    return __builtin_amdgcn_exp2f(scaled ? __builtin_fmaf(h, kLog2e, 64.0f) : h * kLog2e);
+    const float gg = g * g;
+    return __builtin_amdgcn_exp2f(scaled ? __builtin_fmaf(gg, kNegHalfLog2e, 64.0f) : gg * kNegHalfLog2e);
   }
 
   template <bool careful>

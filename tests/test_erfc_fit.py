@@ -64,7 +64,7 @@ def _emulate(which, g):
         r = np.full_like(u, c[-1])
         for ci in c[-2::-1]:
             r = (r * u + ci).astype(f32)
-        gauss = np.exp2((((f32(-0.5) * (g * g)) * l2e) + sc).astype(f32)).astype(f32)
+        gauss = np.exp2((((g * g).astype(f32) * f32(-0.5 * l2e)) + sc).astype(f32)).astype(f32)
         if which == "P":
             e = ((f32(-0.5) * g) * g + (u * r).astype(f32)).astype(f32)
             q = (th * np.exp2((e * l2e + sc).astype(f32))).astype(f32)
