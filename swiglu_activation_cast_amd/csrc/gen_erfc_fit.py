@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-DEGREE = {"P": 8, "Q": 8}
+DEGREE = {"P": 8, "Q": 7}
 NODES = 40001
 
 

@@ -124,16 +124,16 @@ struct ActGeluTanh {
 // P(x) = ln Q(x) are smooth.  Both are evaluated in u = x - 1 = 2t - 2 as
 // P = u R_P(u) and Q = 1 + u R_Q(u), so that erfc(0) = 1 exactly whatever the
 // float32 rounding (tiny gates give the cdf 1/2 exactly, as the definition
-// does).  R_P and R_Q (degree 7, so P and Q have degree 8) are the
-// least-squares fits printed by gen_erfc_fit.py (fit errors 1.5e-6 and
-// 9.9e-7, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
+// does).  R_P (degree 7, so P has degree 8) and R_Q (degree 6, Q degree 7)
+// are the least-squares fits printed by gen_erfc_fit.py (fit errors 1.5e-6
+// and 5.0e-6, relative in erfc), evaluated by Horner's rule.  -z^2 = -g^2 / 2 is
 // exact for a bf16 g.  The forward forms e^(-z^2 + P) with one exponential;
 // the backward forms e^(-z^2) once for both the cdf (times Q) and the
 // Gaussian of the derivative.  Phi(g) is erfc(z) / 2 for g < 0 and
 // 1 - erfc(z) / 2 otherwise.  For g < -8 the exponentials are formed times
 // 2^64 (2^-64 applied last).
 constexpr float kErfcP[8] = {0x1.41b1eep-1f, -0x1.3ad8b8p-4f, -0x1.a4d58ep-6f, -0x1.702f1ep-10f, -0x1.384eb8p-6f, -0x1.9bf628p-7f, -0x1.6f3c04p-9f, -0x1.8cb4e6p-13f};
-constexpr float kErfcQ[8] = {0x1.41bb3ap-1f, 0x1.f23f3cp-4f, -0x1.b16f94p-6f, -0x1.ab2da4p-8f, 0x1.e1a0cap-10f, -0x1.9fa6d2p-10f, -0x1.3db0bcp-10f, -0x1.98ded8p-13f};
+constexpr float kErfcQ[7] = {0x1.41c448p-1f, 0x1.f5cf84p-4f, -0x1.745866p-6f, 0x1.1a637p-10f, 0x1.4bb7c2p-7f, 0x1.bbcf3ap-9f, 0x1.5f16c2p-12f};
 
 struct ActGelu {
   static constexpr float kRsqrt2 = 0.7071067811865476f;
@@ -162,9 +162,10 @@ struct ActGelu {
   __device__ __forceinline__ static float half_erfc_q(float g, float e) {
     const float th = __builtin_amdgcn_rcpf(2.0f + __builtin_fabsf(g) * kRsqrt2);  // t / 2
     const float u = __builtin_fmaf(th, 4.0f, -2.0f);                              // x - 1
-    float r = kErfcQ[7];
+    constexpr int nq = sizeof(kErfcQ) / sizeof(kErfcQ[0]);
+    float r = kErfcQ[nq - 1];
 #pragma unroll
-    for (int i = 6; i >= 0; i--) r = __builtin_fmaf(r, u, kErfcQ[i]);
+    for (int i = nq - 2; i >= 0; i--) r = __builtin_fmaf(r, u, kErfcQ[i]);
     return (th * __builtin_fmaf(u, r, 1.0f)) * e;  // t/2 Q(x) e^(-z^2)
   }
   __device__ __forceinline__ static float cdf_q(float g, float e) {
