@@ -12,7 +12,9 @@
 //             once with row-contiguous 16-byte loads, computes the values,
 //             (optionally) emits the rowwise blocks straight from registers
 //             (full 128-byte lines per row), and writes the values
-//             transposed into LDS.  After one barrier each lane reads 16
+//             transposed into LDS (the SwiGLU backward passes its two output
+//             halves through one LDS tile in turn, which lets three
+//             workgroups share a CU).  After a barrier each lane reads 16
 //             consecutive rows of one column (two 16-byte LDS reads), pairs
 //             with its neighbour lane for the 32-row block amax, and stores
 //             16 E4M3 bytes; eight lanes cover the tile's 128 rows of one
@@ -224,18 +226,36 @@ constexpr int kG = kTM / 16;            // 16-row groups per tile column
 static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0 && (kTC * kG) % kNT == 0, "tile shape");
 
 
-// Static LDS of k_tiled<Op, *>: one transposed bf16 tile per output half.
+// Ops with two output halves (the backward's dgate and dup) whose registers
+// fit the budget of three waves per SIMD (170 VGPRs) pass the halves one
+// after the other through one LDS tile: the workgroup then needs half the
+// LDS, and three workgroups share a CU instead of two.  Others keep one
+// tile per half.
+#ifndef MX_SPLIT_WAVES
+#define MX_SPLIT_WAVES 3
+#endif
 template <class Op>
-constexpr size_t tiled_lds_bytes() {
-  return (size_t)Op::OUT * kTC * kRS * sizeof(uint16_t);
+constexpr int kSplitWaves = 0;
+template <>
+constexpr int kSplitWaves<OpBwd> = MX_SPLIT_WAVES;
+
+template <class Op>
+constexpr int tiled_lds_halves() {
+  return kSplitWaves<Op> > 0 ? 1 : Op::OUT;
 }
 
-// Waves per SIMD that the tile's LDS allows (160 KiB per CU, four waves per
-// workgroup, four SIMDs per CU): the register budget the kernel is held to,
-// so that registers never cut occupancy below what LDS permits.
+// Static LDS of k_tiled<Op, *>: the transposed bf16 tiles it holds at once.
+template <class Op>
+constexpr size_t tiled_lds_bytes() {
+  return (size_t)tiled_lds_halves<Op>() * kTC * kRS * sizeof(uint16_t);
+}
+
+// Waves per SIMD the kernel is compiled for (its register budget): what the
+// tile's LDS allows (160 KiB per CU, four waves per workgroup, four SIMDs
+// per CU), or the split ops' own target.
 template <class Op>
 constexpr int tiled_waves() {
-  return (int)((160 * 1024) / tiled_lds_bytes<Op>());
+  return kSplitWaves<Op> > 0 ? kSplitWaves<Op> : (int)((160 * 1024) / tiled_lds_bytes<Op>());
 }
 
 // Position of tile L (in launch order) of a tiled launch: batch e, first
@@ -321,7 +341,8 @@ __device__ __forceinline__ void group_block_pos(const int32_t *grp, int32_t n, i
 
 template <class Op, bool ROWS, bool GROUPS = false>
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op>(), 8))) void k_tiled(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[Op::OUT][kTC][kRS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[tiled_lds_halves<Op>()][kTC][kRS];
+  constexpr bool kSplit = tiled_lds_halves<Op>() < Op::OUT;
   const TilePos T = tile_pos(a, xcd_remap(blockIdx.x, gridDim.x));
   const int t = threadIdx.x;
 
@@ -375,9 +396,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
     }
   }
 
-  // ---- transpose into LDS: column (8*cc + k), rows kRPT*rg .. +kRPT-1, four at a time
+  // ---- per output half: transpose into LDS (column 8*cc + k, rows
+  // kRPT*rg .. +kRPT-1, four at a time), then the colwise blocks.  Without
+  // the split every half has its own LDS tile and one barrier serves all.
 #pragma unroll
   for (int o = 0; o < Op::OUT; o++) {
+    const int lo = kSplit ? 0 : o;  // LDS tile of this half
+    if (kSplit && o > 0) __syncthreads();  // the previous half's colwise reads are done
 #pragma unroll
     for (int i0 = 0; i0 < kRPT; i0 += 4) {
 #pragma unroll
@@ -392,34 +417,36 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
           p01 = (w0[w] & 0xffffu) | (w1[w] << 16);
           p23 = (w2[w] & 0xffffu) | (w3[w] << 16);
         }
-        *reinterpret_cast<uint2 *>(&lds[o][cc * 8 + k][rg * kRPT + i0]) = make_uint2(p01, p23);
+        *reinterpret_cast<uint2 *>(&lds[lo][cc * 8 + k][rg * kRPT + i0]) = make_uint2(p01, p23);
       }
     }
-  }
-  __syncthreads();
-
-  // ---- colwise: item = (column c, 16-row group g); lanes g, g^1 share a block
+    if (kSplit || o == Op::OUT - 1) {
+      __syncthreads();
+      // ---- colwise: item = (column c, 16-row group g); lanes g, g^1 share a block
 #pragma unroll
-  for (int o = 0; o < Op::OUT; o++) {
+      for (int oc = kSplit ? o : 0; oc <= o; oc++) {
+        const int lc = kSplit ? 0 : oc;
 #pragma unroll
-    for (int p = 0; p < kTC * kG / kNT; p++) {
-      const int i = t + kNT * p;
-      const int g = i % kG, c = i / kG;
-      const V4 v0 = *reinterpret_cast<const V4 *>(&lds[o][c][16 * g]);
-      const V4 v1 = *reinterpret_cast<const V4 *>(&lds[o][c][16 * g + 8]);
-      const u32 v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      u32 am = max_xor1(amax_bits<8>(v));
-      u32 b = e8m0_rceil(am);
-      uint2 q0 = quant8(v, b), q1 = quant8(v + 4, b);
-      if (T.n0 + c < a.N && T.m0 + 16 * g < a.M) {
-        uint8_t *qp = a.q_col + T.e * a.bstride_q + (o * a.N + T.n0) * a.ld_q_col + T.m0;  // uniform
-        store_stream(reinterpret_cast<u32x4_t *>(byte_off(qp, (u32)c * (u32)a.ld_q_col + 16 * g)),
-                     u32x4_t{q0.x, q0.y, q1.x, q1.y});
-        uint8_t *sp = a.s_col + T.e * a.bstride_s + (o * a.N + T.n0) * a.ld_s_col;  // uniform
-        const int k = g >> 1;
-        const u32 sb = GROUPS ? (k == 0 ? gpos[0] : k == 1 ? gpos[1] : k == 2 ? gpos[2] : gpos[3])
-                              : (u32)(T.m0 >> 5) + (u32)k;
-        if ((g & 1) == 0) store_byte(byte_off(sp, (u32)c * (u32)a.ld_s_col + sb), (uint8_t)b);
+        for (int p = 0; p < kTC * kG / kNT; p++) {
+          const int i = t + kNT * p;
+          const int g = i % kG, c = i / kG;
+          const V4 v0 = *reinterpret_cast<const V4 *>(&lds[lc][c][16 * g]);
+          const V4 v1 = *reinterpret_cast<const V4 *>(&lds[lc][c][16 * g + 8]);
+          const u32 v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+          u32 am = max_xor1(amax_bits<8>(v));
+          u32 b = e8m0_rceil(am);
+          uint2 q0 = quant8(v, b), q1 = quant8(v + 4, b);
+          if (T.n0 + c < a.N && T.m0 + 16 * g < a.M) {
+            uint8_t *qp = a.q_col + T.e * a.bstride_q + (oc * a.N + T.n0) * a.ld_q_col + T.m0;  // uniform
+            store_stream(reinterpret_cast<u32x4_t *>(byte_off(qp, (u32)c * (u32)a.ld_q_col + 16 * g)),
+                         u32x4_t{q0.x, q0.y, q1.x, q1.y});
+            uint8_t *sp = a.s_col + T.e * a.bstride_s + (oc * a.N + T.n0) * a.ld_s_col;  // uniform
+            const int k = g >> 1;
+            const u32 sb = GROUPS ? (k == 0 ? gpos[0] : k == 1 ? gpos[1] : k == 2 ? gpos[2] : gpos[3])
+                                  : (u32)(T.m0 >> 5) + (u32)k;
+            if ((g & 1) == 0) store_byte(byte_off(sp, (u32)c * (u32)a.ld_s_col + sb), (uint8_t)b);
+          }
+        }
       }
     }
   }

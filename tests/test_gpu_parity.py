@@ -365,6 +365,51 @@ def test_swiglu_131072x8192_w13_sampled(oracle_mod, c5_inputs, direction):
     _sampled_all_launches(oracle_mod, "swiglu_131072x8192_w13", c5_inputs, direction, 64, 12)
 
 
+# ------------------------------- large ragged both-layout launches, scale strides
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("N", [7200, 7680])
+def test_both_layout_large_ragged_and_scale_strides(oracle_mod, N, direction):
+    """Both-layout launches at 131072 rows with a partial last column tile
+    (N = 7200: 56 whole tiles and one of 32 columns, scale rows of 225 or
+    450 bytes) and with whole tiles (N = 7680).  The both-layout result
+    equals the rowwise and colwise launches bit for bit over the whole
+    output (the rowwise launch is a different kernel), and matches the
+    oracle on sampled slabs.  Rowwise scales written through a padded
+    stride and through an unaligned one equal the packed ones, and the
+    padding bytes are untouched."""
+    dev = _dev()
+    M = 131072
+    print(f"case: both-layout {M}x{N} {direction}", flush=True)
+    inp = synth.swiglu_inputs(M, N, seed=31 + N, std=1.0, device=dev)
+    bwd = direction == "bwd"
+    fn = mx.mxfp8_swiglu_bwd if bwd else mx.mxfp8_swiglu_fwd
+    args = (inp.dh, inp.gate, inp.up) if bwd else (inp.gate, inp.up)
+    W = 2 * N if bwd else N
+    both = fn(*args, rowwise=True, colwise=True)
+    for lay in (ROW, COL):
+        one = fn(*args, **_flags(lay))
+        torch.cuda.synchronize()
+        i, j = (0, 2) if lay == ROW else (1, 3)
+        assert torch.equal(one[i], both[i]) and torch.equal(one[j], both[j]), (N, direction, lay)
+        del one
+    ref = _oracle_slabs(oracle_mod, inp, _slabs(M, 8, N), bwd)
+    st = _compare_slabs(oracle_mod, f"ragged_{N}/{direction}", both, BOTH, ref)
+    assert st.scale_mismatch_rate <= 1e-4, st.record()
+    for extra in (16, 5):  # aligned padding, unaligned stride
+        ld = W // 32 + extra
+        buf = torch.full((M, ld), 0xA5, dtype=torch.uint8, device=dev)
+        q_row, q_col = torch.empty_like(both[0]), torch.empty_like(both[1])
+        s_col = torch.empty_like(both[3])
+        fn(*args, rowwise=True, colwise=True, out=(q_row, q_col, buf[:, :W // 32], s_col))
+        torch.cuda.synchronize()
+        assert torch.equal(buf[:, :W // 32], both[2]), (N, direction, extra)
+        assert (buf[:, W // 32:] == 0xA5).all(), (N, direction, extra)
+        assert torch.equal(q_row, both[0]) and torch.equal(q_col, both[1]) and torch.equal(s_col, both[3])
+        del buf, q_row, q_col, s_col
+    del both, inp
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------- 3D
 def test_quant_3d_small_shapes(oracle_mod):
     dev = _dev()
