@@ -12,9 +12,9 @@
 //             once with row-contiguous 16-byte loads, computes the values,
 //             (optionally) emits the rowwise blocks straight from registers
 //             (full 128-byte lines per row), and writes the values
-//             transposed into LDS (the SwiGLU backward passes its two output
-//             halves through one LDS tile in turn, which lets three
-//             workgroups share a CU).  After a barrier each lane reads 16
+//             transposed into LDS (a both-layout backward passes its two
+//             output halves through one LDS tile in turn where its
+//             registers allow more than two workgroups per CU).  After a barrier each lane reads 16
 //             consecutive rows of one column (two 16-byte LDS reads), pairs
 //             with its neighbour lane for the 32-row block amax, and stores
 //             16 E4M3 bytes; eight lanes cover the tile's 128 rows of one
@@ -226,36 +226,36 @@ constexpr int kG = kTM / 16;            // 16-row groups per tile column
 static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0 && (kTC * kG) % kNT == 0, "tile shape");
 
 
-// Ops with two output halves (the backward's dgate and dup) whose registers
-// fit the budget of three waves per SIMD (170 VGPRs) pass the halves one
-// after the other through one LDS tile: the workgroup then needs half the
-// LDS, and three workgroups share a CU instead of two.  Others keep one
-// tile per half.
-#ifndef MX_SPLIT_WAVES
-#define MX_SPLIT_WAVES 3
-#endif
+// Both-layout launches of ops with two output halves (the backward's dgate
+// and dup) whose registers fit the budget of three waves per SIMD pass the
+// halves one after the other through one LDS tile: the workgroup then needs
+// half the LDS, and three workgroups share a CU instead of two.  Other
+// launches keep one tile per half.
 template <class Op>
 constexpr int kSplitWaves = 0;
 template <>
-constexpr int kSplitWaves<OpBwd> = MX_SPLIT_WAVES;
+constexpr int kSplitWaves<OpBwd> = 3;  // 168 VGPRs
+template <>
+constexpr int kSplitWaves<GatedBwd<ActGelu>> = 3;  // 135, with the folded forms
 
-template <class Op>
+template <class Op, bool ROWS>
 constexpr int tiled_lds_halves() {
-  return kSplitWaves<Op> > 0 ? 1 : Op::OUT;
+  return ROWS && kSplitWaves<Op> > 0 ? 1 : Op::OUT;
 }
 
-// Static LDS of k_tiled<Op, *>: the transposed bf16 tiles it holds at once.
-template <class Op>
+// Static LDS of k_tiled<Op, ROWS>: the transposed bf16 tiles it holds at once.
+template <class Op, bool ROWS>
 constexpr size_t tiled_lds_bytes() {
-  return (size_t)tiled_lds_halves<Op>() * kTC * kRS * sizeof(uint16_t);
+  return (size_t)tiled_lds_halves<Op, ROWS>() * kTC * kRS * sizeof(uint16_t);
 }
 
 // Waves per SIMD the kernel is compiled for (its register budget): what the
 // tile's LDS allows (160 KiB per CU, four waves per workgroup, four SIMDs
-// per CU), or the split ops' own target.
-template <class Op>
+// per CU), or the split launches' own target.
+template <class Op, bool ROWS>
 constexpr int tiled_waves() {
-  return kSplitWaves<Op> > 0 ? kSplitWaves<Op> : (int)((160 * 1024) / tiled_lds_bytes<Op>());
+  return tiled_lds_halves<Op, ROWS>() < Op::OUT ? kSplitWaves<Op>
+                                                : (int)((160 * 1024) / tiled_lds_bytes<Op, ROWS>());
 }
 
 // Position of tile L (in launch order) of a tiled launch: batch e, first
@@ -340,9 +340,9 @@ __device__ __forceinline__ void group_block_pos(const int32_t *grp, int32_t n, i
 }
 
 template <class Op, bool ROWS, bool GROUPS = false>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op>(), 8))) void k_tiled(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[tiled_lds_halves<Op>()][kTC][kRS];
-  constexpr bool kSplit = tiled_lds_halves<Op>() < Op::OUT;
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op, ROWS>(), 8))) void k_tiled(const Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[tiled_lds_halves<Op, ROWS>()][kTC][kRS];
+  constexpr bool kSplit = tiled_lds_halves<Op, ROWS>() < Op::OUT;
   const TilePos T = tile_pos(a, xcd_remap(blockIdx.x, gridDim.x));
   const int t = threadIdx.x;
 
@@ -371,7 +371,12 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
     // token groups: the first 64 group ends, loaded behind the tile's inputs
     if constexpr (GROUPS) r_grp0 = rounded_end(a.grp, a.n_grp, t & 63);
 #pragma unroll
-    for (int i = 0; i < kRPT; i++) Op::apply(in[i], out[i]);
+    for (int i = 0; i < kRPT; i++) {
+      if constexpr (kSplit)
+        Op::apply_lean(in[i], out[i]);
+      else
+        Op::apply(in[i], out[i]);
+    }
   }
   u32 gpos[4] = {0, 0, 0, 0};  // padded positions of the tile's four row blocks (token groups)
   if constexpr (GROUPS) group_block_pos(a.grp, a.n_grp, r_grp0, T.m0, gpos);

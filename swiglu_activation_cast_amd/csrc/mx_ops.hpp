@@ -44,13 +44,16 @@ __device__ __forceinline__ bool any_far(const u32 *g) {
 //   dgate<careful>(da, g)  da * act'(g)   (rounded to bf16 by the caller);
 //   kFarBits               the bf16 pattern above which a chunk takes the
 //                          careful forms (gates so negative that the plain
-//                          fp32 forms would flush a representable result).
+//                          fp32 forms would flush a representable result);
+//   kFolded                whether it also has backward forms that take the
+//                          careful scaling per element, without a branch.
 // The careful forms scale the vanishing exponential by 2^64 and apply 2^-64
 // last, so the only subnormal rounding is the final one.
 
 // silu(g) = g * sigmoid(g); silu'(g) = sigmoid(g) (1 + g (1 - sigmoid(g))).
 struct ActSilu {
   static constexpr u32 kFarBits = 0xC2A0u;  // g < -80
+  static constexpr bool kFolded = false;  // no folded backward forms
 
   template <bool careful>
   __device__ __forceinline__ static float act(float g) {
@@ -81,6 +84,7 @@ struct ActGeluTanh {
   static constexpr float kC1 = 1.5957691216057308f;   // 2 sqrt(2/pi)
   static constexpr float kC3 = 0.07135481627260025f;  // 2 sqrt(2/pi) * 0.044715
   static constexpr u32 kFarBits = 0xC118u;            // g < -9.5 (w < -80 needs g < -9.68)
+  static constexpr bool kFolded = false;  // no folded backward forms
 
   __device__ __forceinline__ static float w(float g) { return g * (kC1 + kC3 * (g * g)); }
   __device__ __forceinline__ static float dw(float g) { return kC1 + 3.0f * kC3 * (g * g); }
@@ -211,6 +215,27 @@ struct ActGelu {
     }
     return r;
   }
+
+  // The same two values with the far-gate scaling taken in every element
+  // instead of in a branch: the exponent gets 64 added and the result is
+  // multiplied by 2^-64 where g < -8, 0 and 1 elsewhere.  fma(x, k, 0)
+  // rounds as x k does (up to the sign of a zero, which the exponential
+  // ignores) and a product with 1 is exact, so each element gets exactly
+  // the value the forms above give it.  A few more instructions per
+  // element, but no branch: the kernel needs far fewer registers.
+  static constexpr bool kFolded = true;
+  __device__ __forceinline__ static float far_bias(float g) { return g < kFarG ? 64.0f : 0.0f; }
+  __device__ __forceinline__ static float far_scale(float g) { return g < kFarG ? k2m64 : 1.0f; }
+  __device__ __forceinline__ static float gauss_b(float g, float bias) {  // e^(-g^2/2) 2^bias
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(g * g, kNegHalfLog2e, bias));
+  }
+  __device__ __forceinline__ static float bwd_act_folded(float g) {
+    return (g * cdf_q(g, gauss_b(g, far_bias(g)))) * far_scale(g);
+  }
+  __device__ __forceinline__ static float dgate_folded(float da, float g) {
+    const float e = gauss_b(g, far_bias(g));
+    return (da * (cdf_q(g, e) + g * (kRsqrt2Pi * e))) * far_scale(g);
+  }
 };
 
 // ReLU: g for g > 0, +0 otherwise (NaN stays NaN); derivative 0 for g <= 0
@@ -218,6 +243,7 @@ struct ActGelu {
 // threshold backward does.
 struct ActRelu {
   static constexpr u32 kFarBits = 0xFFFFu;  // no careful form needed
+  static constexpr bool kFolded = false;  // no folded backward forms
 
   template <bool careful>
   __device__ __forceinline__ static float act(float g) {
@@ -235,6 +261,7 @@ struct ActRelu {
 };
 
 // ------------------------------------------------------------------ gated ops
+
 template <class Act>
 struct GatedFwd {
   static constexpr int IN = 2, OUT = 1;  // in: gate, up
@@ -282,6 +309,25 @@ struct GatedBwd {
     u32 *dg = &out[0].x, *du = &out[1].x;
     eval<false>(dh, g, u, dg, du);
     if (__builtin_expect(any_far<Act::kFarBits>(g), 0)) eval<true>(dh, g, u, dg, du);
+  }
+
+  // apply() for launches held to a tighter register budget: policies with
+  // folded forms (no rare branch) use them, the others take apply().
+  __device__ __forceinline__ static void apply_lean(const V4 *in, V4 *out) {
+    if constexpr (Act::kFolded) {
+      const u32 *dh = &in[0].x, *g = &in[1].x, *u = &in[2].x;
+      u32 *dg = &out[0].x, *du = &out[1].x;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const float g0 = lo_f(g[k]), g1 = hi_f(g[k]), h0 = lo_f(dh[k]), h1 = hi_f(dh[k]);
+        const u32 ap = pack_bf16(Act::bwd_act_folded(g0), Act::bwd_act_folded(g1));
+        du[k] = pack_bf16(h0 * lo_f(ap), h1 * hi_f(ap));
+        const u32 dap = pack_bf16(h0 * lo_f(u[k]), h1 * hi_f(u[k]));
+        dg[k] = pack_bf16(Act::dgate_folded(lo_f(dap), g0), Act::dgate_folded(hi_f(dap), g1));
+      }
+    } else {
+      apply(in, out);
+    }
   }
 };
 

@@ -150,7 +150,7 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, in
       rows ? (const void *)&mx::k_tiled<Op, true, GROUPS> : (const void *)&mx::k_tiled<Op, false, GROUPS>;
   // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
   a.band = (int32_t)std::min<int64_t>(rows ? kBandBoth : kBandCol, n_rt);
-  const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op>());
+  const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op, false>());
   return launch(k, blocks, mx::kNT, a, stream, pad);
 }
 
