@@ -52,14 +52,18 @@ constexpr int64_t kMaxLdOut = (int64_t(1) << 32) / (mx::kTM > mx::kTC ? mx::kTM 
 // tiles in flight extend each q_col output row in long contiguous runs; a
 // both-layout launch also writes rowwise lines, which favour more column
 // tiles in flight, and runs best with bands of 32 (both measured at
-// 131072 x 8192 on MI355X).
+// 131072 x 8192 on MI355X).  Both-layout launches of at most 128 row tiles
+// (each XCD's range then holds at most 16 row tiles of every column) run
+// 1-1.5 points faster with bands of 8 (4096 and 16384 rows, N = 7168);
+// from 256 row tiles on, bands of 32 win by 6-10 points.
 #ifndef MX_BAND_COL
 #define MX_BAND_COL 128
 #endif
 #ifndef MX_BAND_BOTH
 #define MX_BAND_BOTH 32
 #endif
-constexpr int32_t kBandCol = MX_BAND_COL, kBandBoth = MX_BAND_BOTH;
+constexpr int32_t kBandCol = MX_BAND_COL, kBandBoth = MX_BAND_BOTH, kBandBothSmall = 8;
+constexpr int64_t kSmallBandRowTiles = 128;
 
 bool tile_offsets_ok(const int64_t *ld_in, int n_in, int64_t ld_q_row, int64_t ld_s_row, int64_t ld_q_col,
                      int64_t ld_s_col) {
@@ -149,7 +153,8 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, in
   const void *k =
       rows ? (const void *)&mx::k_tiled<Op, true, GROUPS> : (const void *)&mx::k_tiled<Op, false, GROUPS>;
   // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
-  a.band = (int32_t)std::min<int64_t>(rows ? kBandBoth : kBandCol, n_rt);
+  const int64_t band = !rows ? kBandCol : n_rt <= kSmallBandRowTiles ? kBandBothSmall : kBandBoth;
+  a.band = (int32_t)std::min<int64_t>(band, n_rt);
   const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op, false>());
   return launch(k, blocks, mx::kNT, a, stream, pad);
 }
