@@ -12,9 +12,9 @@
 //             once with row-contiguous 16-byte loads, computes the values,
 //             (optionally) emits the rowwise blocks straight from registers
 //             (full 128-byte lines per row), and writes the values
-//             transposed into LDS (a both-layout backward passes its two
-//             output halves through one LDS tile in turn where its
-//             registers allow three workgroups per CU).  After a barrier
+//             transposed into LDS (some both-layout backward launches pass
+//             their two output halves through one LDS tile in turn, so that
+//             three workgroups share a CU).  After a barrier
 //             each lane reads 16 consecutive rows of one column (two
 //             16-byte LDS reads), pairs with its neighbour lane for the
 //             32-row block amax, and stores 16 E4M3 bytes; eight lanes
@@ -228,35 +228,42 @@ static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0 && (kTC * kG) % kN
 
 
 // Both-layout launches of ops with two output halves (the backward's dgate
-// and dup) whose registers fit the budget of three waves per SIMD pass the
-// halves one after the other through one LDS tile: the workgroup then needs
-// half the LDS, and three workgroups share a CU instead of two.  Other
-// launches keep one tile per half.
-template <class Op>
+// and dup) whose registers fit the budget of three waves per SIMD may pass
+// the halves one after the other through one LDS tile: the workgroup then
+// needs half the LDS, and three workgroups share a CU instead of two.
+// Measured (131072 x 8192): the exact-GELU backward (135 VGPRs with its
+// folded forms) and the SwiGLU backward with token groups (168) gain 1-4
+// points on every box; the plain SwiGLU backward gains 2-6 points on some
+// boxes and loses 1.2 on the others, so it keeps one tile per half, as do
+// colwise-only launches (split, their registers spill).
+template <class Op, bool GROUPS>
 constexpr int kSplitWaves = 0;
 template <>
-constexpr int kSplitWaves<OpBwd> = 3;  // 168 VGPRs
+constexpr int kSplitWaves<OpBwd, true> = 3;
 template <>
-constexpr int kSplitWaves<GatedBwd<ActGelu>> = 3;  // 135, with the folded forms
+constexpr int kSplitWaves<GatedBwd<ActGelu>, false> = 3;
+template <>
+constexpr int kSplitWaves<GatedBwd<ActGelu>, true> = 3;
 
-template <class Op, bool ROWS>
+template <class Op, bool ROWS, bool GROUPS>
 constexpr int tiled_lds_halves() {
-  return ROWS && kSplitWaves<Op> > 0 ? 1 : Op::OUT;
+  return ROWS && kSplitWaves<Op, GROUPS> > 0 ? 1 : Op::OUT;
 }
 
-// Static LDS of k_tiled<Op, ROWS>: the transposed bf16 tiles it holds at once.
-template <class Op, bool ROWS>
+// Static LDS of k_tiled<Op, ROWS, GROUPS>: the transposed bf16 tiles it
+// holds at once.
+template <class Op, bool ROWS, bool GROUPS>
 constexpr size_t tiled_lds_bytes() {
-  return (size_t)tiled_lds_halves<Op, ROWS>() * kTC * kRS * sizeof(uint16_t);
+  return (size_t)tiled_lds_halves<Op, ROWS, GROUPS>() * kTC * kRS * sizeof(uint16_t);
 }
 
 // Waves per SIMD the kernel is compiled for (its register budget): what the
 // tile's LDS allows (160 KiB per CU, four waves per workgroup, four SIMDs
 // per CU), or the split launches' own target.
-template <class Op, bool ROWS>
+template <class Op, bool ROWS, bool GROUPS>
 constexpr int tiled_waves() {
-  return tiled_lds_halves<Op, ROWS>() < Op::OUT ? kSplitWaves<Op>
-                                                : (int)((160 * 1024) / tiled_lds_bytes<Op, ROWS>());
+  return tiled_lds_halves<Op, ROWS, GROUPS>() < Op::OUT ? kSplitWaves<Op, GROUPS>
+                                                        : (int)((160 * 1024) / tiled_lds_bytes<Op, ROWS, GROUPS>());
 }
 
 // Position of tile L (in launch order) of a tiled launch: batch e, first
@@ -341,9 +348,10 @@ __device__ __forceinline__ void group_block_pos(const int32_t *grp, int32_t n, i
 }
 
 template <class Op, bool ROWS, bool GROUPS = false>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op, ROWS>(), 8))) void k_tiled(const Args a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[tiled_lds_halves<Op, ROWS>()][kTC][kRS];
-  constexpr bool kSplit = tiled_lds_halves<Op, ROWS>() < Op::OUT;
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves<Op, ROWS, GROUPS>(), 8))) void k_tiled(
+    const Args a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[tiled_lds_halves<Op, ROWS, GROUPS>()][kTC][kRS];
+  constexpr bool kSplit = tiled_lds_halves<Op, ROWS, GROUPS>() < Op::OUT;
   const TilePos T = tile_pos(a, xcd_remap(blockIdx.x, gridDim.x));
   const int t = threadIdx.x;
 

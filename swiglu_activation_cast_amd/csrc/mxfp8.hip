@@ -155,7 +155,7 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, in
   // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
   const int64_t band = !rows ? kBandCol : n_rt <= kSmallBandRowTiles ? kBandBothSmall : kBandBoth;
   a.band = (int32_t)std::min<int64_t>(band, n_rt);
-  const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op, false>());
+  const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op, false, GROUPS>());
   return launch(k, blocks, mx::kNT, a, stream, pad);
 }
 
