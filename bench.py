@@ -247,7 +247,8 @@ def run_sweep():
     """The pages' table on MI355X: fused and unfused time, speedup and
     achieved HBM GB/s for every shape, direction and layout; then the 3D
     expert cast.  Inputs: gate/up the halves of one N(0, 1) bf16 w13 tensor,
-    dh N(0, 1); experts N(0, 0.02)."""
+    dh N(0, 1); experts N(0, 0.02).  Times are medians of 20 launches: at
+    the small shapes one stalled launch would move a mean by a third."""
     import torch
 
     import swiglu_activation_cast_amd as mx
@@ -281,8 +282,8 @@ def run_sweep():
                         mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up, out=v, stream=stream)
                         mx.mxfp8_quant_2d(v, out=out, stream=stream, **fl)
                     nbytes = metrics.swiglu_bwd_bytes(M, N, lay)
-                tu, _ = time_launches(unfused, 20, 10)
-                tf, _ = time_launches(fused, 20, 10)
+                _, tu = time_launches(unfused, 20, 10)
+                _, tf = time_launches(fused, 20, 10)
                 gbps = metrics.gbps(nbytes, tf)
                 print(f"| ({M}, {N}) | {direction} | {lname} | {tu * 1e6:.2f} | {tf * 1e6:.2f} | {tu / tf:.2f}× | "
                       f"{gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% |", flush=True)
@@ -295,7 +296,7 @@ def run_sweep():
         w = synth.expert_weights(E, 8192, 5120, seed=3 + E, device=dev)
         q = torch.empty((E, 5120, 8192), dtype=torch.uint8, device=dev)
         sc = torch.empty((E, 5120, 256), dtype=torch.uint8, device=dev)
-        t, _ = time_launches(lambda: mx.mxfp8_quant_3d_colwise(w, out=(q, sc), stream=stream), 20, 10)
+        _, t = time_launches(lambda: mx.mxfp8_quant_3d_colwise(w, out=(q, sc), stream=stream), 20, 10)
         gbps = metrics.gbps(metrics.quant_3d_bytes(E, 8192, 5120), t)
         print(f"| ({E}, 8192, 5120) | {t * 1e6:.2f} | {gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% |", flush=True)
         del w, q, sc
