@@ -14,12 +14,11 @@
 //             (full 128-byte lines per row), and writes the values
 //             transposed into LDS (some both-layout backward launches pass
 //             their two output halves through one LDS tile in turn, so that
-//             three workgroups share a CU).  After a barrier
-//             each lane reads 16 consecutive rows of one column (two
-//             16-byte LDS reads), pairs with its neighbour lane for the
-//             32-row block amax, and stores 16 E4M3 bytes; eight lanes
-//             cover the tile's 128 rows of one output row, a full 128-byte
-//             line.  Tiles run in bands of
+//             three workgroups share a CU).  After a barrier each lane reads
+//             16 consecutive rows of one column (two 16-byte LDS reads),
+//             pairs with its neighbour lane for the 32-row block amax, and
+//             stores 16 E4M3 bytes; eight lanes cover the tile's 128 rows of
+//             one output row, a full 128-byte line.  Tiles run in bands of
 //             row tiles (row tiles fastest inside a band; the host picks the
 //             band width per launch), and each XCD works through one
 //             contiguous range of tiles, so each 128-byte line of either

@@ -261,7 +261,6 @@ struct ActRelu {
 };
 
 // ------------------------------------------------------------------ gated ops
-
 template <class Act>
 struct GatedFwd {
   static constexpr int IN = 2, OUT = 1;  // in: gate, up
