@@ -50,6 +50,9 @@ struct GemmArgs {
   int32_t scale_vec;
   // K-grouped form: group g's result at c + g * stride_c
   int64_t stride_c;
+  // compute units of the device: the tiles of a last partial round are
+  // split in two when that round would leave at least half of them idle
+  int32_t cus;
 };
 
 // Kernel forms: the plain GEMM; rows of A grouped by device-side offsets
@@ -70,7 +73,6 @@ constexpr int kAhead = 3;             // stages whose loads are issued ahead of 
 constexpr int kGroup = 4;             // tile rows per group in the tile order
 constexpr int kGemmThreads = 256;     // four wavefronts, 2 x 2, each 128 x 128 of C
 constexpr int kSlot = kBM * kBK;      // bytes of one operand in one slot (16 KB)
-constexpr int kLoadsPerStage = 8;     // direct loads per wavefront and stage: 4 of A, 4 of B
 constexpr int kSG = 16;               // scale blocks per LDS scale group
 constexpr int kStagesPerGroup = kSG / (kBK / 32);
 static_assert(kBM == kBN, "the operand load layout assumes square tiles");
@@ -110,15 +112,23 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// One 256-row tile of C, NJ 32-column blocks per wavefront: NJ = 4 is the
+// whole 256 x 256 tile (each wavefront 128 x 128), NJ = 2 one half of it,
+// 256 x 128 (`half` 0 or 1; each wavefront 128 x 64), for the last partial
+// round of tiles.  Every element of C gets the same sum in the same order
+// either way.  L is the tile's index in the tile order over tiles_m rows of
+// tiles (in the grouped form the real count).
+//
 // NT: C written with nontemporal stores (K-long tiles: the stores then do
 // not displace operand lines from L2); otherwise ordinary stores, faster
 // when the tile is short in K.
-template <int MODE, bool NT>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smA[kRing][kSlot], smB[kRing][kSlot];  // [slot]
-  // scale table of one group of kSG blocks: row q < kBM is A's tile row q,
-  // row kBM + q is B's tile row q  [buffer][row][block]
-  __shared__ __attribute__((aligned(1024))) uint8_t smS[2][kBM + kBN][kSG];
+template <int MODE, bool NT, int NJ>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlot], uint8_t (*smB)[kSlot],
+                                          uint8_t (*smS)[kBM + kBN][kSG], const int32_t *offs_s, u32 L, int half,
+                                          int64_t tiles_m) {
+  constexpr int BN = 64 * NJ;     // tile columns
+  constexpr int WBN = 32 * NJ;    // columns per wavefront
+  constexpr int kLoads = 4 + NJ;  // direct loads per wavefront and stage: 4 of A, NJ of B
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
@@ -126,23 +136,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   // Tile order: each XCD takes one contiguous range of tiles; inside it,
   // groups of kGroup tile rows are walked column by column.  In the
   // K-grouped form the tiles of one token group come one after another.
-  u32 L = xcd_remap(blockIdx.x, gridDim.x);
   int64_t kgrp = 0;
   if constexpr (MODE == kGemmGroupK) {
-    const u32 per = (u32)g.tiles_m * (u32)g.tiles_n;
+    const u32 per = (u32)tiles_m * (u32)g.tiles_n;
     kgrp = L / per;
     L %= per;
   }
   const u32 per_group = (u32)kGroup * (u32)g.tiles_n;
   const u32 grp = L / per_group, in_grp = L % per_group;
-  const u32 rows_in_grp = min((u32)kGroup, (u32)g.tiles_m - grp * (u32)kGroup);
+  const u32 rows_in_grp = min((u32)kGroup, (u32)tiles_m - grp * (u32)kGroup);
   const int64_t tm = (int64_t)grp * kGroup + in_grp % rows_in_grp;
-  const int64_t n_base = (int64_t)(in_grp / rows_in_grp) * kBN;
+  const int64_t n_base = (int64_t)(in_grp / rows_in_grp) * kBN + (int64_t)half * BN;
+  if (n_base >= g.N) return;  // the second half of a tile narrower than 128 columns (uniform)
 
   // Rows of this tile: [m_base, m_end).  In the grouped form tile row tm is
   // the (tm - tiles before)-th tile of the group it falls in, counting each
-  // group's tiles from its own first row; the grid holds an upper bound of
-  // tiles (rows / 256 + groups), and tiles past the real count do nothing.
+  // group's tiles from its own first row.
   int64_t m_base = tm * kBM, m_end = g.M;
   const uint8_t *b_mat = g.b, *sb_mat = g.sb;
   // Contraction range [k_lo, k_lo + Kt) of the operands' columns, and the
@@ -150,9 +159,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   int64_t k_lo = 0, Kt = g.K, s_lo = 0;
   float *c_mat = g.c;
   if constexpr (MODE == kGemmGroupM) {
-    __shared__ int32_t offs_s[kMaxGroups];
-    for (int e = t; e < g.G; e += kGemmThreads) offs_s[e] = g.offs[e];
-    __syncthreads();
     int64_t start = 0, before = 0;
     int e_hit = -1;
     for (int e = 0; e < g.G; e++) {  // uniform: every lane walks the same offsets
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     // the walk is uniform; make that visible to the compiler, so that the
     // tile's bases live in scalar registers
     e_hit = __builtin_amdgcn_readfirstlane(e_hit);
-    if (e_hit < 0) return;  // past the real tiles
+    if (e_hit < 0) return;  // past the real tiles (not reached: L < the real count)
     m_base = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((u32)((uint64_t)m_base >> 32)) << 32) |
                        __builtin_amdgcn_readfirstlane((u32)m_base));
     m_end = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((u32)((uint64_t)m_end >> 32)) << 32) |
@@ -198,24 +204,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
 
   // Rows past M (N) are read as the last row: in bounds, never stored.
   const uint8_t *a_tile = g.a + m_base * g.lda + k_lo, *b_tile = b_mat + n_base * g.ldb + k_lo;  // uniform
-  const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, kBN);
+  const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, BN);
   const uint8_t *sa_tile = g.sa + m_base * g.ld_sa + s_lo, *sb_tile = sb_mat + n_base * g.ld_sb + s_lo;  // uniform
   const int64_t nblk = Kt / 32;
   const int nstage = (int)((Kt + kBK - 1) / kBK);
   const int ngroup = (int)((nblk + kSG - 1) / kSG);
 
-  // ---- operand loads.  Slab p = 4 w + q (q = 0..3) of a slot holds tile
-  // rows 16 p .. 16 p + 15; lane l loads row 16 p + l / 4 into stored chunk
-  // l % 4, which holds logical chunk (l % 4) ^ the row's key; the key
-  // (row / 4) % 4 = (l / 16) % 4 is the same for every slab.
+  // ---- operand loads.  Slab p of a slot holds tile rows 16 p .. 16 p + 15:
+  // A's slabs p = 4 w + q (q = 0..3), B's p = 4 w + q as well for a whole
+  // tile and p = 2 w + q (q = 0, 1) for a half; lane l loads row
+  // 16 p + l / 4 into stored chunk l % 4, which holds logical chunk
+  // (l % 4) ^ the row's key; the key (row / 4) % 4 = (l / 16) % 4 is the same
+  // for every slab.
   const u32 kc16 = (((u32)lane & 3u) ^ (((u32)lane >> 4) & 3u)) * 16u;
-  u32 a_roff[4], b_roff[4];
+  auto bslab = [&](int q) { return (u32)(NJ == 4 ? 4 * w + q : 2 * w + q); };
+  u32 a_roff[4], b_roff[NJ];
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const u32 row = 16u * (4u * (u32)w + (u32)q) + ((u32)lane >> 2);
     a_roff[q] = min(row, a_rows - 1) * (u32)g.lda;
-    b_roff[q] = min(row, b_rows - 1) * (u32)g.ldb;
   }
+#pragma unroll
+  for (int q = 0; q < NJ; q++) b_roff[q] = min(16u * bslab(q) + ((u32)lane >> 2), b_rows - 1) * (u32)g.ldb;
   // Stage st goes to slot st % kRing.  Loads of stages past the last re-read
   // the last one into a free slot (never read); chunks at or past K read
   // chunk 0 of their row and are zeroed in LDS before the stage is read.
@@ -234,7 +244,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     for (int q = 0; q < 4; q++) {
       const u32 p = 4u * (u32)w + (u32)q;
       load_lds(ba, a_roff[q] + kc, lds_addr(&smA[slot][p * 1024u]));
-      load_lds(bb, b_roff[q] + kc, lds_addr(&smB[slot][p * 1024u]));
+      if (q < NJ) load_lds(bb, b_roff[q] + kc, lds_addr(&smB[slot][bslab(q) * 1024u]));
     }
   };
   auto zero_tail = [&](int st_) {  // this thread's chunks of stage st_ at or past K -> 0
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
       const u32 p = 4u * (u32)w + (u32)q;
       if ((int64_t)kc16 >= kmax) {
         *reinterpret_cast<u32x4_t *>(&smA[slot][p * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
-        *reinterpret_cast<u32x4_t *>(&smB[slot][p * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
+        if (q < NJ) *reinterpret_cast<u32x4_t *>(&smB[slot][bslab(q) * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
       }
     }
   };
@@ -263,6 +273,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < 2; q++) {
         const u32 trow0 = 64u * (2u * (u32)w + (u32)q);  // uniform: 64 rows of one operand
+        if (trow0 >= (u32)(kBM + BN)) continue;         // past a half tile's B rows
         const u32 trow = trow0 + (u32)lane;
         const bool is_a = trow0 < (u32)kBM;
         const uint8_t *base = is_a ? sa_tile + b0 : sb_tile + b0;
@@ -299,23 +310,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     const u32 sh = 8u * (u32)h + 16u * (u32)(in_g & 1);
 #pragma unroll
     for (int x = 0; x < 4; x++) {
-      const u32 ra = (u32)(wm * 128 + 32 * x + r), rb = (u32)(wn * 128 + 32 * x + r);
+      const u32 ra = (u32)(wm * 128 + 32 * x + r);
       const u32x4_t la = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, (u32)h)]);
       const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, 2u + (u32)h)]);
-      const u32x4_t lb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, (u32)h)]);
-      const u32x4_t hb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, 2u + (u32)h)]);
       o.a[x] = v8i_t{(int)la.x, (int)la.y, (int)la.z, (int)la.w, (int)ha.x, (int)ha.y, (int)ha.z, (int)ha.w};
-      o.b[x] = v8i_t{(int)lb.x, (int)lb.y, (int)lb.z, (int)lb.w, (int)hb.x, (int)hb.y, (int)hb.z, (int)hb.w};
       o.sa[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][ra][4 * (in_g / 2)]) >> sh);
-      o.sb[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][kBM + rb][4 * (in_g / 2)]) >> sh);
+      if (x < NJ) {
+        const u32 rb = (u32)(wn * WBN + 32 * x + r);
+        const u32x4_t lb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, (u32)h)]);
+        const u32x4_t hb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, 2u + (u32)h)]);
+        o.b[x] = v8i_t{(int)lb.x, (int)lb.y, (int)lb.z, (int)lb.w, (int)hb.x, (int)hb.y, (int)hb.z, (int)hb.w};
+        o.sb[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][kBM + rb][4 * (in_g / 2)]) >> sh);
+      }
     }
   };
 
-  v16f_t acc[4][4];
+  v16f_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) acc[i][j] = v16f_t{};
+    for (int j = 0; j < NJ; j++) acc[i][j] = v16f_t{};
 
   // One stage: the MFMAs of stage st from `cur`; between them, the loads of
   // stage st + kAhead (its slot held stage st - 1, whose reads ended before
@@ -332,31 +346,50 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     stage_base(st + kAhead, ba, bb, kc);
     const int lslot = (st + kAhead) & (kRing - 1);
     const int rs = st + 1, rslot = rs & (kRing - 1), rgi = rs / kStagesPerGroup, rin = rs % kStagesPerGroup;
-    u32x4_t la[4], ha[4], lb[4], hb[4];
-    u32 wsa[4], wsb[4];
-#pragma unroll
-    for (int k = 0; k < 16; k++) {
-      const int i = k / 4, j = k % 4;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0, cur.sa[i], 0,
-                                                                   cur.sb[j]);
-      if (k % 2 == 0) {  // load k / 2: A's slab q, then B's
-        const int q = k / 4;
-        const u32 p = 4u * (u32)w + (u32)q;
-        if (k % 4 == 0) load_lds(ba, a_roff[q] + kc, lds_addr(&smA[lslot][p * 1024u]));
-        else load_lds(bb, b_roff[q] + kc, lds_addr(&smB[lslot][p * 1024u]));
-      }
-      const int x = k / 4, part = k % 4;
-      const u32 ra = (u32)(wm * 128 + 32 * x + r), rb = (u32)(wn * 128 + 32 * x + r);
+    u32x4_t la[4], ha[4], lb[NJ], hb[NJ];
+    u32 wsa[4], wsb[NJ];
+    auto read_a = [&](int x, int part) {  // part 0: chunk h and the scale word, 1: chunk 2 + h
+      const u32 ra = (u32)(wm * 128 + 32 * x + r);
       if (part == 0) {
         la[x] = *reinterpret_cast<const u32x4_t *>(&smA[rslot][lds_off(ra, (u32)h)]);
         wsa[x] = *reinterpret_cast<const u32 *>(&smS[rgi & 1][ra][4 * (rin / 2)]);
+      } else {
+        ha[x] = *reinterpret_cast<const u32x4_t *>(&smA[rslot][lds_off(ra, 2u + (u32)h)]);
       }
-      if (part == 1) ha[x] = *reinterpret_cast<const u32x4_t *>(&smA[rslot][lds_off(ra, 2u + (u32)h)]);
-      if (part == 2) {
+    };
+    auto read_b = [&](int x, int part) {
+      const u32 rb = (u32)(wn * WBN + 32 * x + r);
+      if (part == 0) {
         lb[x] = *reinterpret_cast<const u32x4_t *>(&smB[rslot][lds_off(rb, (u32)h)]);
         wsb[x] = *reinterpret_cast<const u32 *>(&smS[rgi & 1][kBM + rb][4 * (rin / 2)]);
+      } else {
+        hb[x] = *reinterpret_cast<const u32x4_t *>(&smB[rslot][lds_off(rb, 2u + (u32)h)]);
       }
-      if (part == 3) hb[x] = *reinterpret_cast<const u32x4_t *>(&smB[rslot][lds_off(rb, 2u + (u32)h)]);
+    };
+#pragma unroll
+    for (int k = 0; k < 4 * NJ; k++) {
+      const int i = k / NJ, j = k % NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0, cur.sa[i], 0,
+                                                                   cur.sb[j]);
+      if constexpr (NJ == 4) {
+        if (k % 2 == 0) {  // load k / 2: A's slab q, then B's
+          const int q = k / 4;
+          const u32 p = 4u * (u32)w + (u32)q;
+          if (k % 4 == 0) load_lds(ba, a_roff[q] + kc, lds_addr(&smA[lslot][p * 1024u]));
+          else load_lds(bb, b_roff[q] + kc, lds_addr(&smB[lslot][p * 1024u]));
+        }
+        const int x = k / 4, part = k % 4;
+        if (part < 2) read_a(x, part);
+        else read_b(x, part - 2);
+      } else {
+        // 8 MFMAs: after each of the first six one load (A's four slabs,
+        // then B's two); after each the reads of one A tile's chunk, and
+        // after the first four also one of B's
+        if (k < 4) load_lds(ba, a_roff[k] + kc, lds_addr(&smA[lslot][(4u * (u32)w + (u32)k) * 1024u]));
+        else if (k < 6) load_lds(bb, b_roff[k - 4] + kc, lds_addr(&smB[lslot][bslab(k - 4) * 1024u]));
+        read_a(k / 2, k % 2);
+        if (k < 4) read_b(k / 2, k % 2);
+      }
       __builtin_amdgcn_sched_barrier(0);  // keep this order: loads and reads spread between the MFMAs
     }
     const u32 sh = 8u * (u32)h + 16u * (u32)(rin & 1);
@@ -364,9 +397,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     for (int x = 0; x < 4; x++) {
       nxt.a[x] = v8i_t{(int)la[x].x, (int)la[x].y, (int)la[x].z, (int)la[x].w,
                        (int)ha[x].x, (int)ha[x].y, (int)ha[x].z, (int)ha[x].w};
+      nxt.sa[x] = (int)(wsa[x] >> sh);
+    }
+#pragma unroll
+    for (int x = 0; x < NJ; x++) {
       nxt.b[x] = v8i_t{(int)lb[x].x, (int)lb[x].y, (int)lb[x].z, (int)lb[x].w,
                        (int)hb[x].x, (int)hb[x].y, (int)hb[x].z, (int)hb[x].w};
-      nxt.sa[x] = (int)(wsa[x] >> sh);
       nxt.sb[x] = (int)(wsb[x] >> sh);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -377,11 +413,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
 #pragma unroll
     for (int x = 0; x < 4; x++) {
 #pragma unroll
-      for (int j = 0; j < 4; j++) asm volatile("" ::"a"(acc[x][j]));
-      asm volatile("" ::"v"(nxt.a[x]), "v"(nxt.b[x]), "v"(nxt.sa[x]), "v"(nxt.sb[x]));
+      for (int j = 0; j < NJ; j++) asm volatile("" ::"a"(acc[x][j]));
+      asm volatile("" ::"v"(nxt.a[x]), "v"(nxt.sa[x]));
+      if (x < NJ) asm volatile("" ::"v"(nxt.b[x]), "v"(nxt.sb[x]));
     }
 #endif
-    wait_vm<kLoadsPerStage>();  // stage st + 2, and scales issued before stage st + kAhead, landed
+    wait_vm<kLoads>();  // stage st + 2, and scales issued before stage st + kAhead, landed
     __syncthreads();
     if ((int64_t)(st + 3) * kBK > Kt && (int64_t)(st + 2) * kBK < Kt) {  // stage st + 2 is the partial last one
       zero_tail(st + 2);
@@ -395,20 +432,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     if (ngroup > 0) load_scales(0);
     load_stage(0);
     load_stage(1);
+    // The first stage body reads the stage after the first one computed:
+    // stage 1 (even stage count) or stage 0 (odd: the leading zero stage
+    // comes first).  Wait until that one, the ones before it and the
+    // scales have landed.
     if (!odd) {
       load_stage(2);
-      wait_vm<2 * kLoadsPerStage>();  // stage 0 and the scales landed
+      wait_vm<kLoads>();  // stages 0 and 1 and the scales landed
     } else {
-      wait_vm<kLoadsPerStage>();
+      wait_vm<kLoads>();  // stage 0 and the scales landed
     }
     __syncthreads();
     if ((int64_t)kBK > Kt) {  // stage 0 is partial (then it is the only one)
       zero_tail(0);
       __syncthreads();
     }
-    if (!odd && (int64_t)2 * kBK > Kt) {  // two stages, the second partial
-      wait_vm<kLoadsPerStage>();
-      __syncthreads();
+    if (!odd && (int64_t)2 * kBK > Kt) {  // two stages, the second partial (landed above)
       zero_tail(1);
       __syncthreads();
     }
@@ -435,30 +474,75 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
     if constexpr (NT) __builtin_nontemporal_store(v, gptr(p));
     else *gptr(p) = v;
   };
-  if (a_rows == (u32)kBM && b_rows == (u32)kBN && g.ldc < (int64_t(1) << 22)) {
+  if (a_rows == (u32)kBM && b_rows == (u32)BN && g.ldc < (int64_t(1) << 22)) {
     // whole tile: a uniform row base per (i, v) and a 32-bit lane offset
     float *c_tile = c_mat + m_base * g.ldc + n_base;
-    const u32 lane_off = ((u32)(wm * 128 + 4 * h) * (u32)g.ldc + (u32)(wn * 128 + r)) * 4u;
+    const u32 lane_off = ((u32)(wm * 128 + 4 * h) * (u32)g.ldc + (u32)(wn * WBN + r)) * 4u;
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
       for (int v = 0; v < 16; v++) {
         float *row_base = c_tile + (int64_t)(32 * i + 8 * (v / 4) + (v % 4)) * g.ldc;
 #pragma unroll
-        for (int j = 0; j < 4; j++) put(byte_off(row_base, lane_off + 128u * (u32)j), acc[i][j][v]);
+        for (int j = 0; j < NJ; j++) put(byte_off(row_base, lane_off + 128u * (u32)j), acc[i][j][v]);
       }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int64_t col = n_base + wn * 128 + 32 * j + r;
+      for (int j = 0; j < NJ; j++) {
+        const int64_t col = n_base + wn * WBN + 32 * j + r;
 #pragma unroll
         for (int v = 0; v < 16; v++) {
           const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
           if (row < m_end && col < g.N) put(c_mat + row * g.ldc + col, acc[i][j][v]);
         }
       }
+  }
+}
+
+// Work items of a launch: the tiles in the tile order, R of them (in the
+// grouped form counted from the device-side offsets, so that the host never
+// reads them; its grid is an upper bound and items past the count exit).
+// With C compute units, the first R - R % C tiles run whole, one round of C
+// after another, in XCD-contiguous ranges.  If the remaining T = R % C tiles
+// would leave at least half the CUs idle in their round (T <= C / 2), they
+// run as 2 T half tiles instead (two consecutive items per tile), which
+// ends that round in a little over half the time.
+template <int MODE, bool NT>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smA[kRing][kSlot], smB[kRing][kSlot];  // [slot]
+  // scale table of one group of kSG blocks: row q < kBM is A's tile row q,
+  // row kBM + q is B's tile row q  [buffer][row][block]
+  __shared__ __attribute__((aligned(1024))) uint8_t smS[2][kBM + kBN][kSG];
+  __shared__ int32_t offs_s[MODE == kGemmGroupM ? kMaxGroups : 1];
+
+  int64_t tiles_m = g.tiles_m;
+  if constexpr (MODE == kGemmGroupM) {
+    for (int e = threadIdx.x; e < g.G; e += kGemmThreads) offs_s[e] = g.offs[e];
+    __syncthreads();
+    // real tile rows: every group's rows rounded up to whole tiles, with the
+    // offsets clamped into ordered groups within [0, M] as the tiles see them
+    int64_t start = 0, n = 0;
+    for (int e = 0; e < g.G; e++) {  // uniform
+      const int64_t end = min<int64_t>(max<int64_t>((int64_t)offs_s[e], start), g.M);
+      n += (end - start + kBM - 1) / kBM;
+      start = end;
+    }
+    tiles_m = n;
+  }
+  const u32 R = (u32)(MODE == kGemmGroupK ? (int64_t)g.G : 1) * (u32)tiles_m * (u32)g.tiles_n;
+  const u32 C = g.cus > 1 ? (u32)g.cus : 1u;
+  const u32 R0 = R - R % C, T = R - R0;
+  const bool split = C > 1 && T > 0 && T <= C / 2;
+  const u32 b = blockIdx.x;
+  if (b >= (split ? R0 + 2 * T : R)) return;  // past the work items (uniform)
+  if (b < R0) {
+    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, xcd_remap(b, R0), 0, tiles_m);
+  } else if (!split) {
+    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, b, 0, tiles_m);
+  } else {
+    gemm_tile<MODE, NT, 2>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 2, (int)((b - R0) & 1u), tiles_m);
   }
 }
 

@@ -478,6 +478,22 @@ mxfp8_status gemm_launch(int mode, const void *a, int64_t lda, const void *sa, i
   if (!mul_ok(tiles_m, tiles_n, &blocks) || (mode == mx::kGemmGroupK && !mul_ok(blocks, G, &blocks)) ||
       blocks > (int64_t)INT32_MAX / mx::kGemmThreads)
     return MXFP8_ERR_OVERFLOW;
+  // The kernel runs a last round of at most half the CUs' worth of tiles as
+  // half tiles (k_mx_gemm): the grid holds those work items, in the
+  // M-grouped form an upper bound (tiles + CUs / 2).  The CU count is the
+  // current device's; it only decides the split, not any result.
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  if (cus > 1) {
+    if (mode == mx::kGemmGroupM) {
+      blocks += cus / 2;
+    } else {
+      const int64_t tail = blocks % cus;
+      if (tail > 0 && tail <= cus / 2) blocks += tail;
+    }
+  }
+  if (blocks > (int64_t)INT32_MAX / mx::kGemmThreads) return MXFP8_ERR_OVERFLOW;
   mx::GemmArgs g{};
   g.a = static_cast<const uint8_t *>(a);
   g.sa = static_cast<const uint8_t *>(sa);
@@ -500,6 +516,7 @@ mxfp8_status gemm_launch(int mode, const void *a, int64_t lda, const void *sa, i
   g.stride_sb = stride_sb;
   g.stride_c = stride_c;
   g.scale_vec = aligned16(sa) && aligned16(sb) && ld_sa % 16 == 0 && ld_sb % 16 == 0 && stride_sb % 16 == 0;
+  g.cus = cus;
   void *kargs[] = {&g};
   // nontemporal C stores for tiles long in K (for the K-grouped form, the
   // mean group length)

@@ -85,6 +85,32 @@ def test_gemm_random_codes(oracle_mod, M, N, K):
     _check(oracle_mod, f"gemm{M}x{N}x{K}", a, sa, b, sb, c.cpu().numpy())
 
 
+def test_gemm_half_tiles_match_whole_tiles(oracle_mod):
+    """A last round of at most half the CUs' worth of 256 x 256 tiles runs as
+    256 x 128 half tiles.  4352 x 4096 (272 tiles) and 4352 x 4352 (289)
+    over the same A put different tiles in that round, so the first 4096
+    columns of the two results come from whole tiles in one launch and half
+    tiles in the other for some elements: they must agree bit for bit (each
+    element is the same sum in the same order).  The last tile row, split
+    in both, is checked against the oracle on sampled rows and columns."""
+    dev = _dev()
+    M, K, N1, N2 = 4352, 512, 4096, 4352
+    print(f"case: gemm half tiles {M}x{N1}/{N2}x{K}", flush=True)
+    rng = np.random.default_rng(77)
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, N2, K)
+    A, SA, B, SB = _to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev)
+    c1 = mx.mxfp8_gemm(A, SA, B[:N1], SB[:N1])
+    c2 = mx.mxfp8_gemm(A, SA, B, SB)
+    torch.cuda.synchronize()
+    assert torch.equal(c2[:, :N1], c1)
+    rows = np.unique(np.concatenate([[0, 4095, 4096, 4223, 4224, M - 1], rng.integers(4096, M, 10),
+                                     rng.integers(0, M, 6)]))
+    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N2 - 129, N2 - 128, N2 - 1], rng.integers(0, N2, 40)]))
+    got = c2.cpu().numpy()[rows][:, cols]
+    _check(oracle_mod, "half_tiles", a[rows], sa[rows], b[cols], sb[cols], got)
+
+
 def test_gemm_on_cast_outputs(oracle_mod):
     """The pipeline the casts serve: A = rowwise cast of x [M, K]; B = the
     colwise cast of w [K, N] (q_col [N, K], s_col [N, K/32]) and, again, the
