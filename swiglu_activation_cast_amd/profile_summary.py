@@ -37,6 +37,7 @@ from . import _build, metrics, synth
 COPY_KERNEL = "k_stream<1, 1,"
 COPY_BYTES = 1 << 30  # the probe's buffers (bench.py stream_ceilings)
 THREADS = 256  # work-items per workgroup of every kernel the bench times
+CUS = 256  # compute units of the MI355X the grids were sized for
 STREAM_CONFIGS = metrics.STREAM_CONFIGS
 
 
@@ -97,6 +98,11 @@ def bench_calls(workload: str, experts: int):
                                        ("wgrad_grouped_gemm_k_8192x5120_t16640_g4", 2, 8192, 5120, 16640, 4)):
         tiles_m = -(-gm // 256) + (G if mode == 1 else 0)
         grid = tiles_m * -(-gn // 256) * (G if mode == 2 else 1)
+        # the launch grid as mxfp8.hip sizes it: a short last round of tiles
+        # runs as half tiles (room for CUS / 2 of them in the grouped form,
+        # whose tile count the host does not know)
+        tail = grid % CUS
+        grid += CUS // 2 if mode == 1 else (tail if 0 < tail <= CUS // 2 else 0)
         rd = gm * gk + gn * gk * (G if mode == 1 else 1)
         calls.append(Call(f"k_mx_gemm<{mode},", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid,
                           2 * gm * gn * gk))
