@@ -111,6 +111,25 @@ def test_gemm_half_tiles_match_whole_tiles(oracle_mod):
     _check(oracle_mod, "half_tiles", a[rows], sa[rows], b[cols], sb[cols], got)
 
 
+def test_gemm_repeated_launches_bit_identical():
+    """Twelve launches of one GEMM (16 stages, an even count, and a last
+    round of half tiles) give the same result bit for bit: a race between
+    the pipeline's loads and its LDS reads shows up as a difference."""
+    dev = _dev()
+    M, N, K = 4352, 4352, 1024
+    print(f"case: gemm repeated launches {M}x{N}x{K}", flush=True)
+    rng = np.random.default_rng(78)
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, N, K)
+    A, SA, B, SB = _to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev)
+    first = mx.mxfp8_gemm(A, SA, B, SB)
+    out = torch.empty_like(first)
+    for _ in range(11):
+        out.fill_(float("nan"))
+        mx.mxfp8_gemm(A, SA, B, SB, out=out)
+        assert torch.equal(out, first)
+
+
 def test_gemm_on_cast_outputs(oracle_mod):
     """The pipeline the casts serve: A = rowwise cast of x [M, K]; B = the
     colwise cast of w [K, N] (q_col [N, K], s_col [N, K/32]) and, again, the
