@@ -27,7 +27,8 @@
 // 16 MFMAs run from registers, the wavefront reads the next stage's operands
 // from LDS into a second register set and issues the loads of the stage
 // three ahead (one after every other MFMA), so that the matrix cores, the
-// LDS and the vector memory unit work at once.
+// LDS and the vector memory unit work at once.  A last round of tiles that
+// would leave at least half the CUs idle runs as 256 x 128 half tiles.
 #pragma once
 #include "mx_kernels.hpp"
 
