@@ -114,6 +114,18 @@ __device__ __forceinline__ float sigmoid_near(float g) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * kLog2e));
 }
 
+// The same sigmoid with one Newton step on the reciprocal: r' = r + r (1 - d r)
+// for d = 1 + e^-g, two fma, which leaves the quotient within about half an
+// ulp.  The hardware reciprocal alone is off by up to about one ulp, enough
+// to round g sigmoid(g) to the other bf16 neighbour where the exact value
+// lies about an ulp from a bf16 rounding midpoint (g = 5.9375 is the one
+// finite bf16 gate where that happens).  Valid for g >= -80, as above.
+__device__ __forceinline__ float sigmoid_refined(float g) {
+  const float d = 1.0f + __builtin_amdgcn_exp2f(-g * kLog2e);
+  const float r = __builtin_amdgcn_rcpf(d);
+  return __builtin_fmaf(__builtin_fmaf(-d, r, 1.0f), r, r);
+}
+
 // For g < -80: sigmoid(g) = e^g / (1 + e^g) and 1 + e^g == 1 in fp32, so
 // sigmoid(g) == e^g, which is below 2^-115 and may be an fp32 subnormal.  It
 // is formed as e^g * 2^64 (a normal number) and the 2^-64 is applied last,

@@ -57,7 +57,7 @@ struct ActSilu {
 
   template <bool careful>
   __device__ __forceinline__ static float act(float g) {
-    float s = g * sigmoid_near(g);
+    float s = g * sigmoid_refined(g);
     if (careful && g < kFar) s = (g * exp_g_times_2p64(g)) * k2m64;
     return s;
   }
@@ -68,10 +68,11 @@ struct ActSilu {
 
   template <bool careful>
   __device__ __forceinline__ static float dgate(float da, float g) {
-    const float sig = sigmoid_near(g);
+    const float sig = sigmoid_refined(g);
     float r = (da * sig) * (1.0f + g * (1.0f - sig));
-    // far-negative gate: sig == e^g, so dg = da * e^g * (1 + g)
-    if (careful && g < kFar) r = ((da * (1.0f + g)) * exp_g_times_2p64(g)) * k2m64;
+    // far-negative gate: sig == e^g, so dg = da * e^g * (1 + g), the small
+    // factors multiplied first: da (1 + g) would overflow for g near -2^127
+    if (careful && g < kFar) r = (((1.0f + g) * exp_g_times_2p64(g)) * da) * k2m64;
     return r;
   }
 };
@@ -112,7 +113,7 @@ struct ActGeluTanh {
     if (careful && wv < kFar) {
       // sigmoid(w) == e^w and 1 - sigmoid(w) == 1: dg = da e^w (1 + g w')
       const float e = exp_g_times_2p64(wv);
-      r = (e == 0.0f) ? da * (g * 0.0f) : ((da * (1.0f + g * d)) * e) * k2m64;
+      r = (e == 0.0f) ? da * (g * 0.0f) : (((1.0f + g * d) * e) * da) * k2m64;
     }
     return r;
   }

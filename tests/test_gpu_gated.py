@@ -148,6 +148,24 @@ def test_gated_exhaustive_gate_values(oracle_mod, act):
     record_rates(f"{act}: every finite bf16 gate, up = dh = 1 [both-layout launch]", "bwd", st2)
 
 
+@pytest.mark.parametrize("act", OTHER)
+def test_gated_exhaustive_gates_wide_upstream(oracle_mod, act):
+    """Every finite bf16 gate with up (2^-20 .. 2^20) and dh (2^-40 .. 2^24)
+    over wide exponent ranges (|da| up to 2^45): no far-negative form may
+    overflow an intermediate for a large da where the exact dgate is
+    finite."""
+    from test_gpu_parity import wide_bf16
+    dev = _dev()
+    print(f"case: gated {act} every finite gate, wide upstream", flush=True)
+    bits = all_bf16_bits()
+    fin = bits[(bits & 0x7FFF) < 0x7F80]
+    fin = np.resize(fin, (fin.size // (32 * 64) + 1) * 32 * 64).reshape(-1, 64)
+    u = wide_bf16(fin.shape, 13, -20, 20)
+    dh = wide_bf16(fin.shape, 14, -40, 24)
+    fwd_check(oracle_mod, "all_gates_wide_fwd", act, fin, u, BOTH, dev)
+    bwd_check(oracle_mod, "all_gates_wide_bwd", act, dh, fin, u, BOTH, dev)
+
+
 # gate ranges where each activation's plain fp32 form would flush a
 # representable result and the careful (2^64-scaled) form takes over
 FAR = {"gelu_tanh": (-10.75, -9.25), "gelu": (-14.0, -7.5), "relu": (-5.0, -0.5)}

@@ -263,6 +263,35 @@ def test_exhaustive_gate_values(oracle_mod):
     record_rates("every finite bf16 gate, up = dh = 1 [both-layout launch]", "bwd", st2)
 
 
+def wide_bf16(shape, seed, emin, emax):
+    """Random bf16 patterns with uniform sign and mantissa and an unbiased
+    exponent uniform in [emin, emax]."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(emin + 127, emax + 128, shape, dtype=np.int64)
+    m = rng.integers(0, 128, shape, dtype=np.int64)
+    sgn = rng.integers(0, 2, shape, dtype=np.int64)
+    return ((sgn << 15) | (e << 7) | m).astype(np.uint16)
+
+
+def test_exhaustive_gates_wide_upstream(oracle_mod):
+    """Every finite bf16 gate with up (2^-20 .. 2^20) and dh (2^-40 .. 2^24)
+    drawn over wide exponent ranges, so that da = dh * up spans 2^-60 ..
+    2^45: the far-negative backward must not overflow an intermediate where
+    the exact dgate is finite (it once formed da (1 + g) first, which is inf
+    for g near -2^127 once |da| > 2, and inf times the vanished exponential
+    gave NaN).  The far forms hold their exponential at 2^64 times its value,
+    which keeps every representable result exact to its last rounding for
+    |da| < 2^49."""
+    dev = _dev()
+    bits = all_bf16_bits()
+    fin = bits[(bits & 0x7FFF) < 0x7F80]
+    fin = np.resize(fin, (fin.size // (32 * 64) + 1) * 32 * 64).reshape(-1, 64)
+    u = wide_bf16(fin.shape, 11, -20, 20)
+    dh = wide_bf16(fin.shape, 12, -40, 24)
+    _fwd_check(oracle_mod, "all_gates_wide_fwd", fin, u, BOTH, dev)
+    _bwd_check(oracle_mod, "all_gates_wide_bwd", dh, fin, u, BOTH, dev)
+
+
 # ------------------------------------------------ full-size, sampled slabs
 def _slabs(M, n, seed):
     rng = np.random.default_rng(seed)
@@ -540,6 +569,33 @@ def test_bf16_values_match_oracle_and_feed_the_plain_cast(oracle_mod, M, N):
         plain = mx.mxfp8_quant_2d(vals, rowwise=True, colwise=True)
         for a, b in zip(fused, plain):
             assert torch.equal(a, b)
+
+
+def test_bf16_values_every_gate(oracle_mod):
+    """The activation-only kernels over every finite bf16 gate (up = dh = 1,
+    so h = du = bf16(silu(g)) and dg = bf16(silu'(g))): h and du equal the
+    exact definition for every gate (the refined reciprocal keeps g = 5.9375,
+    whose exact silu lies about an fp32 ulp below a bf16 rounding midpoint,
+    on the right side); dg within one step, on at most two gates."""
+    dev = _dev()
+    bits = all_bf16_bits()
+    g = np.ascontiguousarray(bits[(bits & 0x7FFF) < 0x7F80].reshape(-1, 32))
+    one = np.full_like(g, 0x3F80)
+    gd, od = _to_dev(g, dev), _to_dev(one, dev)
+    h = torch_bf16_to_bits(mx.mxfp8_swiglu_fwd_bf16(gd, od))
+    y = torch_bf16_to_bits(mx.mxfp8_swiglu_bwd_bf16(od, gd, od))
+    dg_o, du_o = oracle_mod.swiglu_bwd_values(one, g, one)
+    h_o = oracle_mod.swiglu_fwd_values(g, one)
+
+    def steps(a, b):
+        d = np.abs(a.astype(np.int32) - b.astype(np.int32))
+        d[((a & 0x7FFF) == 0) & ((b & 0x7FFF) == 0)] = 0  # +0 and -0
+        return d
+
+    assert steps(h, h_o).max() == 0, int((steps(h, h_o) > 0).sum())
+    assert steps(y[:, 32:], du_o).max() == 0
+    d = steps(y[:, :32], dg_o)
+    assert d.max() <= 1 and (d > 0).sum() <= 2, int((d > 0).sum())
 
 
 def test_bf16_values_strided_output():
