@@ -120,16 +120,25 @@ __device__ __forceinline__ void wait_vm() {
 // either way.  L is the tile's index in the tile order over tiles_m rows of
 // tiles (in the grouped form the real count).
 //
+// The tile's 32-row blocks alternate between the two wavefront rows
+// (wavefront row wm takes blocks wm, wm + 2, wm + 4, wm + 6), so that a
+// short tile (a group's last rows, or the last rows of A) has rows in both
+// wavefront rows.  NI is the number of those blocks each wavefront
+// computes: 4 for a tile of more than 128 rows, 2 for at most 128, 1 for at
+// most 64.  A tile of 64 rows then takes 4 MFMAs per stage and wavefront
+// instead of 16; its loads are the same.
+//
 // NT: C written with nontemporal stores (K-long tiles: the stores then do
 // not displace operand lines from L2); otherwise ordinary stores, faster
 // when the tile is short in K.
-template <int MODE, bool NT, int NJ>
+template <int MODE, bool NT, int NJ, int NI = 4>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlot], uint8_t (*smB)[kSlot],
                                           uint8_t (*smS)[kBM + kBN][kSG], const int32_t *offs_s, u32 L, int half,
                                           int64_t tiles_m) {
+  const u32 L_in = L;
   constexpr int BN = 64 * NJ;     // tile columns
   constexpr int WBN = 32 * NJ;    // columns per wavefront
-  constexpr int kLoads = 4 + NJ;  // direct loads per wavefront and stage: 4 of A, NJ of B
+  constexpr int kLoads = NI + NJ;  // direct loads per wavefront and stage: NI of A, NJ of B
   const int t = threadIdx.x, lane = t & 63;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = w >> 1, wn = w & 1, r = lane & 31, h = lane >> 5;
@@ -206,25 +215,33 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
   // Rows past M (N) are read as the last row: in bounds, never stored.
   const uint8_t *a_tile = g.a + m_base * g.lda + k_lo, *b_tile = b_mat + n_base * g.ldb + k_lo;  // uniform
   const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, BN);
+  if constexpr (NI == 4) {
+    if (a_rows <= 2u * 32u) {  // uniform: a short tile, one row block per wavefront
+      gemm_tile<MODE, NT, NJ, 1>(g, smA, smB, smS, offs_s, L_in, half, tiles_m);
+      return;
+    }
+    if (a_rows <= 4u * 32u) {  // two row blocks per wavefront
+      gemm_tile<MODE, NT, NJ, 2>(g, smA, smB, smS, offs_s, L_in, half, tiles_m);
+      return;
+    }
+  }
   const uint8_t *sa_tile = g.sa + m_base * g.ld_sa + s_lo, *sb_tile = sb_mat + n_base * g.ld_sb + s_lo;  // uniform
   const int64_t nblk = Kt / 32;
   const int nstage = (int)((Kt + kBK - 1) / kBK);
   const int ngroup = (int)((nblk + kSG - 1) / kSG);
 
   // ---- operand loads.  Slab p of a slot holds tile rows 16 p .. 16 p + 15:
-  // A's slabs p = 4 w + q (q = 0..3), B's p = 4 w + q as well for a whole
-  // tile and p = 2 w + q (q = 0, 1) for a half; lane l loads row
-  // 16 p + l / 4 into stored chunk l % 4, which holds logical chunk
-  // (l % 4) ^ the row's key; the key (row / 4) % 4 = (l / 16) % 4 is the same
-  // for every slab.
+  // A's slabs p = NI w + q (q < NI: the 64 NI rows the wavefronts compute),
+  // B's p = 4 w + q for a whole tile and p = 2 w + q (q = 0, 1) for a half;
+  // lane l loads row 16 p + l / 4 into stored chunk l % 4, which holds
+  // logical chunk (l % 4) ^ the row's key; the key (row / 4) % 4 =
+  // (l / 16) % 4 is the same for every slab.
   const u32 kc16 = (((u32)lane & 3u) ^ (((u32)lane >> 4) & 3u)) * 16u;
+  auto aslab = [&](int q) { return (u32)(NI * w + q); };
   auto bslab = [&](int q) { return (u32)(NJ == 4 ? 4 * w + q : 2 * w + q); };
-  u32 a_roff[4], b_roff[NJ];
+  u32 a_roff[NI], b_roff[NJ];
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const u32 row = 16u * (4u * (u32)w + (u32)q) + ((u32)lane >> 2);
-    a_roff[q] = min(row, a_rows - 1) * (u32)g.lda;
-  }
+  for (int q = 0; q < NI; q++) a_roff[q] = min(16u * aslab(q) + ((u32)lane >> 2), a_rows - 1) * (u32)g.lda;
 #pragma unroll
   for (int q = 0; q < NJ; q++) b_roff[q] = min(16u * bslab(q) + ((u32)lane >> 2), b_rows - 1) * (u32)g.ldb;
   // Stage st goes to slot st % kRing.  Loads of stages past the last re-read
@@ -243,9 +260,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     const int slot = st_ & (kRing - 1);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const u32 p = 4u * (u32)w + (u32)q;
-      load_lds(ba, a_roff[q] + kc, lds_addr(&smA[slot][p * 1024u]));
-      if (q < NJ) load_lds(bb, b_roff[q] + kc, lds_addr(&smB[slot][bslab(q) * 1024u]));
+      if (q < NI) load_lds(ba, a_roff[q < NI ? q : 0] + kc, lds_addr(&smA[slot][aslab(q) * 1024u]));
+      if (q < NJ) load_lds(bb, b_roff[q < NJ ? q : 0] + kc, lds_addr(&smB[slot][bslab(q) * 1024u]));
     }
   };
   auto zero_tail = [&](int st_) {  // this thread's chunks of stage st_ at or past K -> 0
@@ -253,9 +269,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     const int slot = st_ & (kRing - 1);
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const u32 p = 4u * (u32)w + (u32)q;
       if ((int64_t)kc16 >= kmax) {
-        *reinterpret_cast<u32x4_t *>(&smA[slot][p * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
+        if (q < NI) *reinterpret_cast<u32x4_t *>(&smA[slot][aslab(q) * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
         if (q < NJ) *reinterpret_cast<u32x4_t *>(&smB[slot][bslab(q) * 1024u + 16u * (u32)lane]) = u32x4_t{0, 0, 0, 0};
       }
     }
@@ -311,11 +326,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     const u32 sh = 8u * (u32)h + 16u * (u32)(in_g & 1);
 #pragma unroll
     for (int x = 0; x < 4; x++) {
-      const u32 ra = (u32)(wm * 128 + 32 * x + r);
-      const u32x4_t la = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, (u32)h)]);
-      const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, 2u + (u32)h)]);
-      o.a[x] = v8i_t{(int)la.x, (int)la.y, (int)la.z, (int)la.w, (int)ha.x, (int)ha.y, (int)ha.z, (int)ha.w};
-      o.sa[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][ra][4 * (in_g / 2)]) >> sh);
+      if (x < NI) {
+        const u32 ra = (u32)(32 * (2 * x + wm) + r);
+        const u32x4_t la = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, (u32)h)]);
+        const u32x4_t ha = *reinterpret_cast<const u32x4_t *>(&smA[slot][lds_off(ra, 2u + (u32)h)]);
+        o.a[x] = v8i_t{(int)la.x, (int)la.y, (int)la.z, (int)la.w, (int)ha.x, (int)ha.y, (int)ha.z, (int)ha.w};
+        o.sa[x] = (int)(*reinterpret_cast<const u32 *>(&smS[gi & 1][ra][4 * (in_g / 2)]) >> sh);
+      }
       if (x < NJ) {
         const u32 rb = (u32)(wn * WBN + 32 * x + r);
         const u32x4_t lb = *reinterpret_cast<const u32x4_t *>(&smB[slot][lds_off(rb, (u32)h)]);
@@ -326,9 +343,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     }
   };
 
-  v16f_t acc[4][NJ];
+  v16f_t acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < NI; i++)
 #pragma unroll
     for (int j = 0; j < NJ; j++) acc[i][j] = v16f_t{};
 
@@ -350,7 +367,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     u32x4_t la[4], ha[4], lb[NJ], hb[NJ];
     u32 wsa[4], wsb[NJ];
     auto read_a = [&](int x, int part) {  // part 0: chunk h and the scale word, 1: chunk 2 + h
-      const u32 ra = (u32)(wm * 128 + 32 * x + r);
+      const u32 ra = (u32)(32 * (2 * x + wm) + r);
       if (part == 0) {
         la[x] = *reinterpret_cast<const u32x4_t *>(&smA[rslot][lds_off(ra, (u32)h)]);
         wsa[x] = *reinterpret_cast<const u32 *>(&smS[rgi & 1][ra][4 * (rin / 2)]);
@@ -370,32 +387,43 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
 #pragma unroll
     for (int k = 0; k < 4 * NJ; k++) {
       const int i = k / NJ, j = k % NJ;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[i], cur.b[j], acc[i][j], 0, 0, 0, cur.sa[i], 0,
-                                                                   cur.sb[j]);
+      if (i < NI) {  // resolved at compile time: the loop is unrolled
+        const int ii = i < NI ? i : NI - 1;
+        acc[ii][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.a[ii], cur.b[j], acc[ii][j], 0, 0, 0,
+                                                                      cur.sa[ii], 0, cur.sb[j]);
+      }
       if constexpr (NJ == 4) {
-        if (k % 2 == 0) {  // load k / 2: A's slab q, then B's
+        if (k % 2 == 0) {  // load k / 2: A's slab q (if it has one), then B's
           const int q = k / 4;
-          const u32 p = 4u * (u32)w + (u32)q;
-          if (k % 4 == 0) load_lds(ba, a_roff[q] + kc, lds_addr(&smA[lslot][p * 1024u]));
-          else load_lds(bb, b_roff[q] + kc, lds_addr(&smB[lslot][p * 1024u]));
+          if (k % 4 == 0) {
+            if (q < NI) load_lds(ba, a_roff[q < NI ? q : 0] + kc, lds_addr(&smA[lslot][aslab(q) * 1024u]));
+          } else {
+            load_lds(bb, b_roff[q] + kc, lds_addr(&smB[lslot][bslab(q) * 1024u]));
+          }
         }
         const int x = k / 4, part = k % 4;
-        if (part < 2) read_a(x, part);
-        else read_b(x, part - 2);
+        if (part < 2) {
+          if (x < NI) read_a(x, part);
+        } else {
+          read_b(x, part - 2);
+        }
       } else {
         // 8 MFMAs: after each of the first six one load (A's four slabs,
         // then B's two); after each the reads of one A tile's chunk, and
         // after the first four also one of B's
-        if (k < 4) load_lds(ba, a_roff[k] + kc, lds_addr(&smA[lslot][(4u * (u32)w + (u32)k) * 1024u]));
-        else if (k < 6) load_lds(bb, b_roff[k - 4] + kc, lds_addr(&smB[lslot][bslab(k - 4) * 1024u]));
-        read_a(k / 2, k % 2);
+        if (k < 4) {
+          if (k < NI) load_lds(ba, a_roff[k < NI ? k : 0] + kc, lds_addr(&smA[lslot][aslab(k) * 1024u]));
+        } else if (k < 6) {
+          load_lds(bb, b_roff[k - 4] + kc, lds_addr(&smB[lslot][bslab(k - 4) * 1024u]));
+        }
+        if (k / 2 < NI) read_a(k / 2, k % 2);
         if (k < 4) read_b(k / 2, k % 2);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep this order: loads and reads spread between the MFMAs
     }
     const u32 sh = 8u * (u32)h + 16u * (u32)(rin & 1);
 #pragma unroll
-    for (int x = 0; x < 4; x++) {
+    for (int x = 0; x < NI; x++) {
       nxt.a[x] = v8i_t{(int)la[x].x, (int)la[x].y, (int)la[x].z, (int)la[x].w,
                        (int)ha[x].x, (int)ha[x].y, (int)ha[x].z, (int)ha[x].w};
       nxt.sa[x] = (int)(wsa[x] >> sh);
@@ -413,9 +441,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     // past the barrier, where nothing overlaps them.
 #pragma unroll
     for (int x = 0; x < 4; x++) {
+      if (x < NI) {
 #pragma unroll
-      for (int j = 0; j < NJ; j++) asm volatile("" ::"a"(acc[x][j]));
-      asm volatile("" ::"v"(nxt.a[x]), "v"(nxt.sa[x]));
+        for (int j = 0; j < NJ; j++) asm volatile("" ::"a"(acc[x < NI ? x : 0][j]));
+        asm volatile("" ::"v"(nxt.a[x]), "v"(nxt.sa[x]));
+      }
       if (x < NJ) asm volatile("" ::"v"(nxt.b[x]), "v"(nxt.sb[x]));
     }
 #endif
@@ -478,24 +508,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
   if (a_rows == (u32)kBM && b_rows == (u32)BN && g.ldc < (int64_t(1) << 22)) {
     // whole tile: a uniform row base per (i, v) and a 32-bit lane offset
     float *c_tile = c_mat + m_base * g.ldc + n_base;
-    const u32 lane_off = ((u32)(wm * 128 + 4 * h) * (u32)g.ldc + (u32)(wn * WBN + r)) * 4u;
+    const u32 lane_off = ((u32)(32 * wm + 4 * h) * (u32)g.ldc + (u32)(wn * WBN + r)) * 4u;
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < NI; i++)
 #pragma unroll
       for (int v = 0; v < 16; v++) {
-        float *row_base = c_tile + (int64_t)(32 * i + 8 * (v / 4) + (v % 4)) * g.ldc;
+        float *row_base = c_tile + (int64_t)(64 * i + 8 * (v / 4) + (v % 4)) * g.ldc;
 #pragma unroll
         for (int j = 0; j < NJ; j++) put(byte_off(row_base, lane_off + 128u * (u32)j), acc[i][j][v]);
       }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < NI; i++)
 #pragma unroll
       for (int j = 0; j < NJ; j++) {
         const int64_t col = n_base + wn * WBN + 32 * j + r;
 #pragma unroll
         for (int v = 0; v < 16; v++) {
-          const int64_t row = m_base + wm * 128 + 32 * i + 8 * (v / 4) + 4 * h + (v % 4);
+          const int64_t row = m_base + 32 * (2 * i + wm) + 8 * (v / 4) + 4 * h + (v % 4);
           if (row < m_end && col < g.N) put(c_mat + row * g.ldc + col, acc[i][j][v]);
         }
       }
