@@ -111,6 +111,45 @@ def test_gemm_half_tiles_match_whole_tiles(oracle_mod):
     _check(oracle_mod, "half_tiles", a[rows], sa[rows], b[cols], sb[cols], got)
 
 
+@pytest.mark.parametrize("tail", [1, 32, 64, 65, 128, 129])
+def test_gemm_short_tiles_match_whole_tiles(oracle_mod, tail):
+    """A last tile of at most 64 (128) rows runs in the form whose
+    wavefronts compute one (two) row blocks each and load only those rows.
+    Its rows must equal, bit for bit, the same rows computed inside whole
+    tiles: A's first 1024 + tail rows against all 1280 rows (the tail rows
+    at 1024.. fall in a short tile in the first launch and in a whole tile
+    in the second; 160 tiles, so no half tiles in either).  Then the
+    grouped form with two groups ending in short tiles (192 whole-width
+    tiles) against the plain GEMM of each group's rows (96 tiles, all run
+    as half tiles)."""
+    dev = _dev()
+    M, N, K = 1280, 8192, 640
+    print(f"case: gemm short tiles, tail {tail}", flush=True)
+    rng = np.random.default_rng(300 + tail)
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, N, K)
+    A, SA, B, SB = _to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev)
+    m = 1024 + tail
+    c_short = mx.mxfp8_gemm(A[:m], SA[:m], B, SB)
+    c_whole = mx.mxfp8_gemm(A, SA, B, SB)
+    torch.cuda.synchronize()
+    assert torch.equal(c_short, c_whole[:m])
+    rows = np.unique(np.concatenate([[1024, m - 1], rng.integers(1024, m, 6)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 20)]))
+    _check(oracle_mod, f"short_tail{tail}", a[rows], sa[rows], b[cols], sb[cols], c_short.cpu().numpy()[rows][:, cols])
+    # two groups of 512 + tail rows, each against expert b (the same matrix twice)
+    g1 = 512 + tail
+    offs = torch.tensor([g1, 2 * g1], dtype=torch.int32, device=dev)
+    Ag = torch.cat([A[:g1], A[:g1]])
+    SAg = torch.cat([SA[:g1], SA[:g1]])
+    Bg = torch.stack([B, B])
+    SBg = torch.stack([SB, SB])
+    cg = mx.mxfp8_grouped_gemm(Ag, SAg, Bg, SBg, offs)
+    c_plain = mx.mxfp8_gemm(A[:g1], SA[:g1], B, SB)
+    torch.cuda.synchronize()
+    assert torch.equal(cg[:g1], c_plain) and torch.equal(cg[g1:], c_plain)
+
+
 def test_gemm_repeated_launches_bit_identical():
     """Twelve launches of one GEMM (16 stages, an even count, and a last
     round of half tiles) give the same result bit for bit: a race between
