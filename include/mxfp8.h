@@ -206,7 +206,9 @@ mxfp8_status mxfp8_swiglu_bwd_bf16(const void *dh, int64_t ld_dh, const void *ga
  * b 16-byte aligned.  Scales may sit at any byte offset; scale rows that
  * start 16-byte aligned (sa, sb, ld_sa, ld_sb, and stride_sb in the grouped
  * form, all multiples of 16, as the casts' outputs are when K is a multiple
- * of 512) are fetched 16 bytes at a time, others byte by byte (slower).
+ * of 512) are fetched 16 bytes at a time straight into shared memory,
+ * others as 4-byte words through registers (a little slower), and the
+ * blocks of a last group of fewer than 16 byte by byte.
  * A NaN code or a scale byte of 255 makes the sums it enters NaN.
  */
 mxfp8_status mxfp8_gemm(const void *a, int64_t lda, const void *sa, int64_t ld_sa,

@@ -279,8 +279,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
   // ---- scales, kSG blocks (kStagesPerGroup stages) at a time, into buffer
   // group % 2.  Full groups of 16-byte-aligned scale rows go global -> LDS
   // directly: wavefront w fills table rows 128 w .. 128 w + 127, lane l one
-  // row.  Otherwise thread t reads A's and B's tile row t byte by byte,
-  // blocks past K / 32 reading 127 (2^0) against zero data.
+  // row.  Otherwise thread t reads A's and B's tile row t: a full group
+  // as 4-byte words, the last partial one byte by byte, blocks past K / 32
+  // reading 127 (2^0) against zero data.
   auto group_vec = [&](int gi) { return g.scale_vec && (int64_t)(gi + 1) * kSG <= nblk; };
   const u32 sa_row = min((u32)t, a_rows - 1), sb_row = min((u32)t, b_rows - 1);
   auto load_scales = [&](int gi) {
@@ -296,7 +297,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
         const u32 off = is_a ? min(trow, a_rows - 1) * (u32)g.ld_sa : min(trow - kBM, b_rows - 1) * (u32)g.ld_sb;
         load_lds(base, off, lds_addr(&smS[gi & 1][trow0][0]));
       }
-    } else {
+    } else if ((int64_t)(gi + 1) * kSG <= nblk) {
+      // A whole group of scale rows that are not 16-byte aligned: thread t
+      // takes the 16 bytes of A's and B's tile row t from the five 4-byte
+      // words around them (the fifth only where the bytes are not word
+      // aligned; each word read holds at least one of the row's bytes, so no
+      // read reaches a page the row does not touch), joined by v_alignbyte.
+      auto row16 = [&](const uint8_t *p) {
+        const u32 sft = (u32)((uintptr_t)p & 3u);
+        const u32 *q = reinterpret_cast<const u32 *>((uintptr_t)p - sft);
+        const u32 d0 = *gptr(q), d1 = *gptr(q + 1), d2 = *gptr(q + 2), d3 = *gptr(q + 3);
+        const u32 d4 = *gptr(q + (sft ? 4 : 3));
+        return u32x4_t{__builtin_amdgcn_alignbyte(d1, d0, sft), __builtin_amdgcn_alignbyte(d2, d1, sft),
+                       __builtin_amdgcn_alignbyte(d3, d2, sft), __builtin_amdgcn_alignbyte(d4, d3, sft)};
+      };
+      const u32x4_t va = row16(byte_off(sa_tile + b0, sa_row * (u32)g.ld_sa));
+      const u32x4_t vb = row16(byte_off(sb_tile + b0, sb_row * (u32)g.ld_sb));
+      *reinterpret_cast<u32x4_t *>(&smS[gi & 1][t][0]) = va;
+      *reinterpret_cast<u32x4_t *>(&smS[gi & 1][kBM + t][0]) = vb;
+    } else {  // the last, partial group: byte by byte, blocks past K / 32 as 127 (2^0)
       u32 wa[4] = {0, 0, 0, 0}, wb[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < kSG; j++) {

@@ -150,6 +150,40 @@ def test_gemm_short_tiles_match_whole_tiles(oracle_mod, tail):
     assert torch.equal(cg[:g1], c_plain) and torch.equal(cg[g1:], c_plain)
 
 
+@pytest.mark.parametrize("K,shift", [(4160, 0), (1088, 1), (1600, 3), (1056, 2)])
+def test_gemm_unaligned_scale_rows_match_aligned(oracle_mod, K, shift):
+    """Scale rows that do not start 16-byte aligned (packed rows of K/32
+    bytes, the table starting `shift` bytes into its buffer) are read as
+    4-byte words, and a last group of fewer than 16 blocks byte by byte.
+    The result must equal, bit for bit, the same GEMM with its scale rows
+    padded to 16-byte aligned starts (read straight into shared memory)."""
+    dev = _dev()
+    M, N = 600, 520
+    print(f"case: gemm unaligned scale rows K={K} shift={shift}", flush=True)
+    rng = np.random.default_rng(K + shift)
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, N, K)
+    A, B = _to_dev(a, dev), _to_dev(b, dev)
+
+    def placed(s, ld, off):
+        rows, w = s.shape
+        buf = torch.zeros(off + rows * ld + 16, dtype=torch.uint8, device=dev)
+        view = buf[off:off + rows * ld].view(rows, ld)[:, :w]
+        view.copy_(torch.from_numpy(s).to(dev))
+        return view
+
+    kb = K // 32
+    pad = -(-kb // 16) * 16
+    c_aligned = mx.mxfp8_gemm(A, placed(sa, pad, 0), B, placed(sb, pad, 0))
+    c_packed = mx.mxfp8_gemm(A, placed(sa, kb, shift), B, placed(sb, kb, shift))
+    torch.cuda.synchronize()
+    assert torch.equal(c_packed, c_aligned)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 6)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 12)]))
+    _check(oracle_mod, f"unaligned_scales_K{K}", a[rows], sa[rows], b[cols], sb[cols],
+           c_packed.cpu().numpy()[rows][:, cols])
+
+
 def test_gemm_repeated_launches_bit_identical():
     """Twelve launches of one GEMM (16 stages, an even count, and a last
     round of half tiles) give the same result bit for bit: a race between
