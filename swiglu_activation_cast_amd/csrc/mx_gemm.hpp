@@ -588,7 +588,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   const u32 b = blockIdx.x;
   if (b >= (split ? R0 + 2 * T : R)) return;  // past the work items (uniform)
   if (b < R0) {
-    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, xcd_remap(b, R0), 0, tiles_m);
+    u32 L = xcd_remap(b, R0);
+    if constexpr (MODE == kGemmGroupK) {
+      // The groups' tiles differ in depth, and each XCD takes a fixed
+      // eighth of the work items (the dispatcher deals workgroups to the
+      // XCDs in turn), so a contiguous eighth per XCD would leave the XCDs
+      // holding the deepest group working while the others idle.  When the
+      // counts divide, XCD x takes instead the x-th eighth of every group,
+      // each eighth a contiguous run of that group's tile order.
+      const u32 per = (u32)tiles_m * (u32)g.tiles_n, share = per / 8u, range = R0 / 8u;
+      if (R0 % 8u == 0 && per % 8u == 0 && range == share * (u32)g.G) {
+        const u32 x = L / range, p = L % range;
+        L = (p / share) * per + x * share + p % share;
+      }
+    }
+    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, L, 0, tiles_m);
   } else if (!split) {
     gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, b, 0, tiles_m);
   } else {
