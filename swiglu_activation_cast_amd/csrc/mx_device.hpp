@@ -65,12 +65,16 @@ __device__ __forceinline__ u32 max_xor2(u32 v) {
 // amax = (1 + m/128) 2^(e-127).  448 * 2^k = 1.75 * 2^(k+8), so the least
 // k with amax <= 448 * 2^k is e-135 when m <= 0x60 (mantissa <= 1.75) and
 // e-134 otherwise; byte = k + 127, floored at 0 (zero and subnormal amax and
-// tiny normals all land on byte 0).  The largest finite bf16 gives 247.
+// tiny normals all land on byte 0).  The largest finite bf16 gives 247; a
+// non-finite amax (a >= 0x7f80) gives 255.
+// In five instructions: a + 0x1f carries into the exponent field exactly
+// when m > 0x60, so the byte is ((a + 0x1f) >> 7) - 8; a + 0x80 reaches bit
+// 15 exactly when a >= 0x7f80, and adding that bit to a lifts the byte past
+// 255, where the clamp to [0, 255] holds it.  Equal to the rule above for
+// every a in [0, 0x7fff] (checked exhaustively).
 __device__ __forceinline__ u32 e8m0_rceil(u32 a) {
-  int e = (int)(a >> 7);
-  int b = e - 8 + ((a & 0x7fu) > 0x60u ? 1 : 0);
-  b = b < 0 ? 0 : b;
-  return a >= 0x7f80u ? 255u : (u32)b;
+  const int y = (int)(a + ((a + 0x80u) & 0x8000u)) + (0x1f - 0x400);
+  return (u32)min(max(y >> 7, 0), 255);
 }
 
 // ---------------------------------------------------------------- E4M3 cast
@@ -88,8 +92,15 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float e8m0_as_scale(u32 b) { return __uint_as_float(b << 23); }
 
 // Four bf16 values (two packed words) -> four codes, byte i = element i.
+// Each convert replaces one 16-bit half of its destination and keeps the
+// other; the two together replace both, so the destination may start as any
+// value.  REUSE starts it as w0, whose register the first convert then takes
+// over where the values are not needed afterwards (a zero start costs a
+// move); elsewhere it starts at zero, which leaves the register allocator
+// more freedom.
+template <bool REUSE = false>
 __device__ __forceinline__ u32 cvt4(u32 w0, u32 w1, float scale) {
-  i16x2 r = {0, 0};
+  i16x2 r = REUSE ? __builtin_bit_cast(i16x2, w0) : i16x2{0, 0};
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w0), scale, false);
   r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, w1), scale, true);
   return __builtin_bit_cast(u32, r);
@@ -97,9 +108,10 @@ __device__ __forceinline__ u32 cvt4(u32 w0, u32 w1, float scale) {
 
 // Quantize eight values of a block (four packed words) with scale byte b;
 // b == 255 marks an invalid (NaN/Inf) block, whose codes are all 0x7F.
+template <bool REUSE = false>
 __device__ __forceinline__ uint2 quant8(const u32 *v, u32 b) {
   const float s = e8m0_as_scale(b);
-  uint2 q = make_uint2(cvt4(v[0], v[1], s), cvt4(v[2], v[3], s));
+  uint2 q = make_uint2(cvt4<REUSE>(v[0], v[1], s), cvt4<REUSE>(v[2], v[3], s));
   if (b == 255u) q = make_uint2(0x7f7f7f7fu, 0x7f7f7f7fu);
   return q;
 }

@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256) void k_rowwise(const Args a) {
       for (int o = 0; o < Op::OUT; o++) {
         u32 am = max_xor2(max_xor1(amax_bits<4>(&out[o].x)));
         u32 b = e8m0_rceil(am);
-        uint2 q = quant8(&out[o].x, b);
+        uint2 q = quant8<true>(&out[o].x, b);
         if (c < nch) {
           const int64_t col = o * a.N + c * 8;
           store_stream(reinterpret_cast<unsigned long long *>(qr + col), ((unsigned long long)q.y << 32) | q.x);
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(tiled_waves
           const u32 v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
           u32 am = max_xor1(amax_bits<8>(v));
           u32 b = e8m0_rceil(am);
-          uint2 q0 = quant8(v, b), q1 = quant8(v + 4, b);
+          uint2 q0 = quant8<true>(v, b), q1 = quant8<true>(v + 4, b);
           if (T.n0 + c < a.N && T.m0 + 16 * g < a.M) {
             uint8_t *qp = a.q_col + T.e * a.bstride_q + (oc * a.N + T.n0) * a.ld_q_col + T.m0;  // uniform
             store_stream(reinterpret_cast<u32x4_t *>(byte_off(qp, (u32)c * (u32)a.ld_q_col + 16 * g)),
