@@ -28,7 +28,9 @@
 // from LDS into a second register set and issues the loads of the stage
 // three ahead (one after every other MFMA), so that the matrix cores, the
 // LDS and the vector memory unit work at once.  A last round of tiles that
-// would leave at least half the CUs idle runs as 256 x 128 half tiles.
+// would leave at least half the CUs idle runs as 256 x 128 half tiles, and
+// a tile of at most 128 rows computes and loads only the row blocks that
+// can hold its rows.  Unaligned scale rows are read as 4-byte words.
 #pragma once
 #include "mx_kernels.hpp"
 
