@@ -127,8 +127,8 @@ __device__ __forceinline__ void wait_vm() {
 // short tile (a group's last rows, or the last rows of A) has rows in both
 // wavefront rows.  NI is the number of those blocks each wavefront
 // computes: 4 for a tile of more than 128 rows, 2 for at most 128, 1 for at
-// most 64.  A tile of 64 rows then takes 4 MFMAs per stage and wavefront
-// instead of 16; its loads are the same.
+// most 64.  A tile of 64 rows then takes 4 MFMAs and 5 loads per stage and
+// wavefront instead of 16 and 8 (only the A rows it computes are loaded).
 //
 // NT: C written with nontemporal stores (K-long tiles: the stores then do
 // not displace operand lines from L2); otherwise ordinary stores, faster
@@ -147,7 +147,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
 
   // Tile order: each XCD takes one contiguous range of tiles; inside it,
   // groups of kGroup tile rows are walked column by column.  In the
-  // K-grouped form the tiles of one token group come one after another.
+  // K-grouped form L runs over the groups one after another (the kernel
+  // hands each XCD an eighth of every group).
   int64_t kgrp = 0;
   if constexpr (MODE == kGemmGroupK) {
     const u32 per = (u32)tiles_m * (u32)g.tiles_n;
