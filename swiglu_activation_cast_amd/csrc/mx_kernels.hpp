@@ -232,9 +232,9 @@ static_assert(kRPT % 4 == 0 && kTM % 32 == 0 && kCPR % 4 == 0 && (kTC * kG) % kN
 // needs half the LDS, and three workgroups share a CU instead of two.
 // Measured (131072 x 8192): the exact-GELU backward (135 VGPRs with its
 // folded forms) and the SwiGLU backward with token groups (168) gain 1-4
-// points on every box; the plain SwiGLU backward gains 2-6 points on some
-// boxes and loses 1.2 on the others, so it keeps one tile per half, as do
-// colwise-only launches (split, their registers spill).
+// points on every MI355X measured; the plain SwiGLU backward gains 2-6
+// points on some and loses about 1 on most, so it keeps one tile per half,
+// as do colwise-only launches (split, their registers spill).
 template <class Op, bool GROUPS>
 constexpr int kSplitWaves = 0;
 template <>
