@@ -1,6 +1,6 @@
 """Seeded random cases of the casts against the oracle (GPU).
 
-Each case draws an operation (the plain cast, the SwiGLU forward or
+The 2D cases: each draws an operation (the plain cast, the SwiGLU forward or
 backward, or a gated forward or backward with another activation), a launch
 layout, a shape and padded input row strides from its own seed, so that the
 cases reach the tile-order paths the fixed-shape tests meet only at large
@@ -8,6 +8,10 @@ sizes: bands of 8, 32 and 128 row tiles, each with a ragged last band, one
 ragged last row tile and one ragged last column tile, and inputs read
 through row strides wider than the row ("Add swiglu + MXFP8 fused CuTe DSL
 kernel", Summary: the packed w13 input whose halves are gate and up).
+
+The 3D cases draw expert counts, shapes and padded strides; the grouped
+cases draw token-group ends (unsorted, negative, past the end, empty
+groups).
 
 Same bar as the fixed-shape tests: the plain cast bit-exact, the fused casts
 within oracle/parity.py's tolerance (codes within one E4M3 step, scales
@@ -123,6 +127,60 @@ def test_random_case(oracle_mod, idx):
         orc = oracle_mod.gated_bwd(dh, g, u, layout, oa)
         vals = np.concatenate(oracle_mod.gated_bwd_values(dh, g, u, oa), axis=1)
     compare_fused(oracle_mod, name, _gpu(outs), orc, vals, layout)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("idx", range(12))
+def test_random_3d_case(oracle_mod, idx):
+    """The 3D per-expert colwise cast ("[mxfp8 moe training] update 3d quant
+    colwise scaling kernel ...", Summary) on a drawn expert count, shape and
+    padded expert and row strides: bit-exact against the oracle."""
+    dev = _dev()
+    rng = np.random.default_rng(9500 + idx)
+    E, N, K = int(rng.integers(1, 13)), 32 * int(rng.integers(1, 13)), 8 * int(rng.integers(1, 41))
+    pn, pk = int(rng.integers(0, 3)), 8 * int(rng.integers(0, 3))
+    print(f"case 3d {idx}: E={E} N={N} K={K} row pad {pk} expert pad {pn} rows", flush=True)
+    w = torch_bf16_to_bits(synth.expert_weights(E, N + pn, K + pk, seed=int(rng.integers(1 << 30)), std=1.0))
+    w_dev = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to(dev)[:, :N, :K]
+    q, s_ = mx.mxfp8_quant_3d_colwise(w_dev)
+    qo, so = oracle_mod.quant_3d_colwise(np.ascontiguousarray(w[:, :N, :K]))
+    assert_exact(f"q3d#{idx}", q.cpu().numpy(), qo)
+    assert_exact(f"s3d#{idx}", s_.cpu().numpy(), so)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("idx", range(12))
+def test_random_grouped_cast(oracle_mod, idx):
+    """The casts with token groups on drawn group ends (sorted or not, some
+    negative, some past the end, empty groups, up to 80 groups): every
+    output equals the ungrouped cast's, and the colwise scales sit where
+    the oracle's per-group padded layout puts them."""
+    from test_gpu_grouped import _expected_padded
+    dev = _dev()
+    rng = np.random.default_rng(9700 + idx)
+    kind = ("quant", "fwd", "bwd")[idx % 3]
+    M, N, G = 32 * int(rng.integers(1, 400)), 32 * int(rng.integers(1, 6)), int(rng.integers(1, 81))
+    ends = np.sort(rng.integers(-40, M + 100, G))
+    if rng.random() < 0.3:
+        rng.shuffle(ends)
+    offs = [int(e) for e in ends]
+    print(f"case grouped {idx}: {kind} M={M} N={N} G={G}", flush=True)
+    offs_t = torch.tensor(offs, dtype=torch.int32, device=dev)
+    inp = synth.swiglu_inputs(M, N, seed=int(rng.integers(1 << 30)), std=2.0, device=dev)
+    if kind == "quant":
+        grouped = mx.mxfp8_quant_2d_grouped(inp.gate, offs_t, rowwise=True, colwise=True)
+        plain = mx.mxfp8_quant_2d(inp.gate, rowwise=True, colwise=True)
+    elif kind == "fwd":
+        grouped = mx.mxfp8_gated_fwd_grouped(inp.gate, inp.up, offs_t, rowwise=True, colwise=True)
+        plain = mx.mxfp8_swiglu_fwd(inp.gate, inp.up, rowwise=True, colwise=True)
+    else:
+        grouped = mx.mxfp8_gated_bwd_grouped(inp.dh, inp.gate, inp.up, offs_t, rowwise=True, colwise=True)
+        plain = mx.mxfp8_swiglu_bwd(inp.dh, inp.gate, inp.up, rowwise=True, colwise=True)
+    for i, name in ((0, "q_row"), (1, "q_col"), (2, "s_row")):
+        assert torch.equal(grouped[i], plain[i]), name
+    s_pad = grouped[3].cpu().numpy()
+    assert s_pad.shape[1] == M // 32 + 16 * G
+    assert_exact(f"s_col padded#{idx}", s_pad, _expected_padded(oracle_mod, plain[3].cpu().numpy(), M, offs, s_pad.shape[1]))
 
 
 def test_cases_reach_every_band():
