@@ -11,7 +11,7 @@ kernel", Summary: the packed w13 input whose halves are gate and up).
 
 The 3D cases draw expert counts, shapes and padded strides; the grouped
 cases draw token-group ends (unsorted, negative, past the end, empty
-groups).
+groups), for the grouped casts and for the K-grouped GEMM.
 
 Same bar as the fixed-shape tests: the plain cast bit-exact, the fused casts
 within oracle/parity.py's tolerance (codes within one E4M3 step, scales
@@ -181,6 +181,21 @@ def test_random_grouped_cast(oracle_mod, idx):
     s_pad = grouped[3].cpu().numpy()
     assert s_pad.shape[1] == M // 32 + 16 * G
     assert_exact(f"s_col padded#{idx}", s_pad, _expected_padded(oracle_mod, plain[3].cpu().numpy(), M, offs, s_pad.shape[1]))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("idx", range(10))
+def test_random_grouped_gemm_k(oracle_mod, idx):
+    """The K-grouped GEMM (the weight gradient over token groups) on drawn
+    token counts and group ends, through the same check as its fixed cases
+    (every group against the oracle, empty groups zero)."""
+    from test_gpu_grouped import test_grouped_gemm_k_random as check_case
+    rng = np.random.default_rng(9900 + idx)
+    T, G = 32 * int(rng.integers(1, 121)), int(rng.integers(1, 13))
+    ends = np.sort(rng.integers(-40, T + 100, G))
+    if rng.random() < 0.3:
+        rng.shuffle(ends)
+    check_case(oracle_mod, T, [int(e) for e in ends])
 
 
 def test_cases_reach_every_band():
