@@ -132,6 +132,11 @@ mxfp8_status launch(const void *kernel, int64_t blocks, int threads, const Args 
 // per CU, more than 160 KiB / (cap + 1) per workgroup leaves room for `cap`.
 constexpr int64_t kLdsPerCu = 160 * 1024;
 constexpr int64_t kCapTiles2d = 32768, kCapTiles3d = 40960;  // grid sizes where the caps were measured to pay
+// Both-layout launches of the fused forward (gate and up in, one output
+// half) fit four workgroups per CU; three stream faster on grids of at
+// least 4096 tiles (131072 x 8192: +0.7 points, 16384 x 7168: +1.2), while
+// 4096 x 2048 (512 tiles) loses a point and the plain cast gains nothing.
+constexpr int64_t kCapTilesFwdBoth = 4096;
 
 unsigned lds_pad_for_cap(int cap, size_t static_lds) {
   if (cap <= 0) return 0;
@@ -141,7 +146,7 @@ unsigned lds_pad_for_cap(int cap, size_t static_lds) {
 
 // Launch of the colwise / both-layout kernel over `batches` stacked [M, N]
 // problems (batches > 1 only for the 3D cast); `cap` is the workgroups per
-// CU for a colwise-only launch (0: as many as fit).
+// CU (0: as many as fit).
 template <class Op, bool GROUPS = false>
 mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, int cap = 0) {
   const int64_t n_rt = (a.M + mx::kTM - 1) / mx::kTM, n_ct = (a.N + mx::kTC - 1) / mx::kTC;
@@ -155,7 +160,8 @@ mxfp8_status launch_colwise(Args a, bool rows, int64_t batches, void *stream, in
   // band <= n_rt keeps band * n_ct (computed in 32 bits in the kernel) <= per
   const int64_t band = !rows ? kBandCol : n_rt <= kSmallBandRowTiles ? kBandBothSmall : kBandBoth;
   a.band = (int32_t)std::min<int64_t>(band, n_rt);
-  const unsigned pad = rows ? 0u : lds_pad_for_cap(cap, mx::tiled_lds_bytes<Op, false, GROUPS>());
+  const unsigned pad =
+      lds_pad_for_cap(cap, rows ? mx::tiled_lds_bytes<Op, true, GROUPS>() : mx::tiled_lds_bytes<Op, false, GROUPS>());
   return launch(k, blocks, mx::kNT, a, stream, pad);
 }
 
@@ -199,9 +205,11 @@ mxfp8_status dispatch_2d(const Args &a, int layout, void *stream) {
     return launch((const void *)&mx::k_rowwise<Op, kRowUnroll>, blocks, 256, a, stream);
   }
   const int64_t tiles = ((a.M + mx::kTM - 1) / mx::kTM) * ((a.N + mx::kTC - 1) / mx::kTC);
-  const int cap = tiles >= kCapTiles2d ? 2 : 0;
-  if (a.n_grp > 0) return launch_colwise<Op, true>(a, layout == MXFP8_BOTH, 1, stream, cap);
-  return launch_colwise<Op>(a, layout == MXFP8_BOTH, 1, stream, cap);
+  const bool both = layout == MXFP8_BOTH;
+  const bool fused_fwd = Op::IN == 2 && Op::OUT == 1;
+  const int cap = !both ? (tiles >= kCapTiles2d ? 2 : 0) : (fused_fwd && tiles >= kCapTilesFwdBoth ? 3 : 0);
+  if (a.n_grp > 0) return launch_colwise<Op, true>(a, both, 1, stream, cap);
+  return launch_colwise<Op>(a, both, 1, stream, cap);
 }
 
 // Checks of the token-group arguments of the grouped casts: 1..kMaxGroups
