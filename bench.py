@@ -86,9 +86,21 @@ def measured_traffic(src_hash: str, kernel: str):
     return int(v) if v is not None else None
 
 
-def time_launches(fn, iters, warmup):
-    """Average duration (s) of fn's launch, HIP events on torch's current
-    stream (the stream the binding launches on)."""
+# Spin cycles that hold the stream while the host queues a timed series
+# (a few milliseconds at the shader clock): far longer than the host needs
+# to enqueue 20 launches with their events.
+BACKLOG_CYCLES = 5_000_000
+
+
+def time_launches(fn, iters, warmup, backlog=False):
+    """Average and median duration (s) of fn's launch, HIP events on torch's
+    current stream (the stream the binding launches on).
+
+    With backlog, the stream first runs a short spin kernel, so every launch
+    and event of the series is queued before the first one starts and the
+    launches run back to back: the events then time the kernels alone.
+    Without it, a launch shorter than the host's time per call (about 14 us
+    from Python) is timed with the host's gap before it."""
     import torch
 
     for _ in range(warmup):
@@ -96,6 +108,8 @@ def time_launches(fn, iters, warmup):
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
     torch.cuda.synchronize()
+    if backlog:
+        torch.cuda._sleep(BACKLOG_CYCLES)
     for i in range(iters):
         starts[i].record()
         fn()
@@ -247,8 +261,11 @@ def run_sweep():
     """The pages' table on MI355X: fused and unfused time, speedup and
     achieved HBM GB/s for every shape, direction and layout; then the 3D
     expert cast.  Inputs: gate/up the halves of one N(0, 1) bf16 w13 tensor,
-    dh N(0, 1); experts N(0, 0.02).  Times are medians of 20 launches: at
-    the small shapes one stalled launch would move a mean by a third."""
+    dh N(0, 1); experts N(0, 0.02).  Times are medians of 20 launches run
+    back to back behind a spin kernel (kernel time; at the small shapes one
+    stalled launch would move a mean by a third); the last column times the
+    same fused call launched from Python one at a time, the host's
+    overhead included."""
     import torch
 
     import swiglu_activation_cast_amd as mx
@@ -257,8 +274,9 @@ def run_sweep():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    print("| input_shape (M, K) | direction | scales | unfused µs | fused µs | speedup | fused GB/s | % of 8 TB/s |")
-    print("|---|---|---|---|---|---|---|---|")
+    print("| input_shape (M, K) | direction | scales | unfused µs | fused µs | speedup | fused GB/s | % of 8 TB/s "
+          "| fused µs per call from Python |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for M, N in SWEEP_SHAPES:
         inp = synth.swiglu_inputs(M, N, seed=5, std=1.0, packed=True, device=dev)
         outs = {"forward": mx.alloc_outputs(M, N, mx.BOTH, dev), "backward": mx.alloc_outputs(M, 2 * N, mx.BOTH, dev)}
@@ -282,11 +300,12 @@ def run_sweep():
                         mx.mxfp8_swiglu_bwd_bf16(inp.dh, inp.gate, inp.up, out=v, stream=stream)
                         mx.mxfp8_quant_2d(v, out=out, stream=stream, **fl)
                     nbytes = metrics.swiglu_bwd_bytes(M, N, lay)
-                _, tu = time_launches(unfused, 20, 10)
-                _, tf = time_launches(fused, 20, 10)
+                _, tu = time_launches(unfused, 20, 10, backlog=True)
+                _, tf = time_launches(fused, 20, 10, backlog=True)
+                _, tc = time_launches(fused, 20, 10)
                 gbps = metrics.gbps(nbytes, tf)
                 print(f"| ({M}, {N}) | {direction} | {lname} | {tu * 1e6:.2f} | {tf * 1e6:.2f} | {tu / tf:.2f}× | "
-                      f"{gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% |", flush=True)
+                      f"{gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% | {tc * 1e6:.2f} |", flush=True)
         del inp, outs, vals
         torch.cuda.empty_cache()
     print()
@@ -296,7 +315,7 @@ def run_sweep():
         w = synth.expert_weights(E, 8192, 5120, seed=3 + E, device=dev)
         q = torch.empty((E, 5120, 8192), dtype=torch.uint8, device=dev)
         sc = torch.empty((E, 5120, 256), dtype=torch.uint8, device=dev)
-        _, t = time_launches(lambda: mx.mxfp8_quant_3d_colwise(w, out=(q, sc), stream=stream), 20, 10)
+        _, t = time_launches(lambda: mx.mxfp8_quant_3d_colwise(w, out=(q, sc), stream=stream), 20, 10, backlog=True)
         gbps = metrics.gbps(metrics.quant_3d_bytes(E, 8192, 5120), t)
         print(f"| ({E}, 8192, 5120) | {t * 1e6:.2f} | {gbps:.1f} | {100 * gbps / metrics.HBM_PEAK_GBPS:.1f}% |", flush=True)
         del w, q, sc
