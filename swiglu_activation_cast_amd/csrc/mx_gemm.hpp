@@ -28,7 +28,8 @@
 // from LDS into a second register set and issues the loads of the stage
 // three ahead (one after every other MFMA), so that the matrix cores, the
 // LDS and the vector memory unit work at once.  A last round of tiles that
-// would leave at least half the CUs idle runs as 256 x 128 half tiles, and
+// would leave at least half the CUs idle runs as 256 x 128 half tiles (at
+// least three quarters idle: 256 x 64 quarter tiles), and
 // a tile of at most 128 rows computes and loads only the row blocks that
 // can hold its rows.  Unaligned scale rows are read as 4-byte words.
 #pragma once
@@ -54,7 +55,8 @@ struct GemmArgs {
   // K-grouped form: group g's result at c + g * stride_c
   int64_t stride_c;
   // compute units of the device: the tiles of a last partial round are
-  // split in two when that round would leave at least half of them idle
+  // split in two when that round would leave at least half of them idle,
+  // in four when at least three quarters
   int32_t cus;
 };
 
@@ -117,9 +119,10 @@ __device__ __forceinline__ void wait_vm() {
 
 // One 256-row tile of C, NJ 32-column blocks per wavefront: NJ = 4 is the
 // whole 256 x 256 tile (each wavefront 128 x 128), NJ = 2 one half of it,
-// 256 x 128 (`half` 0 or 1; each wavefront 128 x 64), for the last partial
-// round of tiles.  Every element of C gets the same sum in the same order
-// either way.  L is the tile's index in the tile order over tiles_m rows of
+// 256 x 128, and NJ = 1 one quarter, 256 x 64 (`half`: which half or
+// quarter; each wavefront 128 x 32 NJ), for the last partial round of
+// tiles.  Every element of C gets the same sum in the same order either
+// way.  L is the tile's index in the tile order over tiles_m rows of
 // tiles (in the grouped form the real count).
 //
 // The tile's 32-row blocks alternate between the two wavefront rows
@@ -235,13 +238,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
 
   // ---- operand loads.  Slab p of a slot holds tile rows 16 p .. 16 p + 15:
   // A's slabs p = NI w + q (q < NI: the 64 NI rows the wavefronts compute),
-  // B's p = 4 w + q for a whole tile and p = 2 w + q (q = 0, 1) for a half;
+  // B's p = NJ w + q (q < NJ: 4 per wavefront for a whole tile, 2 for a
+  // half, 1 for a quarter);
   // lane l loads row 16 p + l / 4 into stored chunk l % 4, which holds
   // logical chunk (l % 4) ^ the row's key; the key (row / 4) % 4 =
   // (l / 16) % 4 is the same for every slab.
   const u32 kc16 = (((u32)lane & 3u) ^ (((u32)lane >> 4) & 3u)) * 16u;
   auto aslab = [&](int q) { return (u32)(NI * w + q); };
-  auto bslab = [&](int q) { return (u32)(NJ == 4 ? 4 * w + q : 2 * w + q); };
+  auto bslab = [&](int q) { return (u32)(NJ * w + q); };
   u32 a_roff[NI], b_roff[NJ];
 #pragma unroll
   for (int q = 0; q < NI; q++) a_roff[q] = min(16u * aslab(q) + ((u32)lane >> 2), a_rows - 1) * (u32)g.lda;
@@ -429,7 +433,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
         } else {
           read_b(x, part - 2);
         }
-      } else {
+      } else if constexpr (NJ == 2) {
         // 8 MFMAs: after each of the first six one load (A's four slabs,
         // then B's two); after each the reads of one A tile's chunk, and
         // after the first four also one of B's
@@ -440,6 +444,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
         }
         if (k / 2 < NI) read_a(k / 2, k % 2);
         if (k < 4) read_b(k / 2, k % 2);
+      } else {
+        // 4 MFMAs: after the first B's slab; after each A's slab k (if it
+        // has one) and both chunks of A tile k; after the first two one
+        // chunk of B's
+        if (k == 0) load_lds(bb, b_roff[0] + kc, lds_addr(&smB[lslot][bslab(0) * 1024u]));
+        if (k < NI) {
+          load_lds(ba, a_roff[k < NI ? k : 0] + kc, lds_addr(&smA[lslot][aslab(k) * 1024u]));
+          read_a(k, 0);
+          read_a(k, 1);
+        }
+        if (k < 2) read_b(0, k);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep this order: loads and reads spread between the MFMAs
     }
@@ -560,8 +575,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
 // With C compute units, the first R - R % C tiles run whole, one round of C
 // after another, in XCD-contiguous ranges.  If the remaining T = R % C tiles
 // would leave at least half the CUs idle in their round (T <= C / 2), they
-// run as 2 T half tiles instead (two consecutive items per tile), which
-// ends that round in a little over half the time.
+// run as 2 T half tiles instead (two consecutive items per tile), and as
+// 4 T quarter tiles if at least three quarters (T <= C / 4): that round
+// then ends in a little over half (a quarter of) the time.
 template <int MODE, bool NT>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smA[kRing][kSlot], smB[kRing][kSlot];  // [slot]
@@ -587,9 +603,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   const u32 R = (u32)(MODE == kGemmGroupK ? (int64_t)g.G : 1) * (u32)tiles_m * (u32)g.tiles_n;
   const u32 C = g.cus > 1 ? (u32)g.cus : 1u;
   const u32 R0 = R - R % C, T = R - R0;
-  const bool split = C > 1 && T > 0 && T <= C / 2;
+  const u32 parts = C <= 1 || T == 0 ? 1u : T <= C / 4 ? 4u : T <= C / 2 ? 2u : 1u;  // items per last-round tile
   const u32 b = blockIdx.x;
-  if (b >= (split ? R0 + 2 * T : R)) return;  // past the work items (uniform)
+  if (b >= R0 + parts * T) return;  // past the work items (uniform)
   if (b < R0) {
     u32 L = xcd_remap(b, R0);
     if constexpr (MODE == kGemmGroupK) {
@@ -606,10 +622,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
       }
     }
     gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, L, 0, tiles_m);
-  } else if (!split) {
+  } else if (parts == 1) {
     gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, b, 0, tiles_m);
-  } else {
+  } else if (parts == 2) {
     gemm_tile<MODE, NT, 2>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 2, (int)((b - R0) & 1u), tiles_m);
+  } else {
+    gemm_tile<MODE, NT, 1>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 4, (int)((b - R0) & 3u), tiles_m);
   }
 }
 

@@ -486,19 +486,22 @@ mxfp8_status gemm_launch(int mode, const void *a, int64_t lda, const void *sa, i
   if (!mul_ok(tiles_m, tiles_n, &blocks) || (mode == mx::kGemmGroupK && !mul_ok(blocks, G, &blocks)) ||
       blocks > (int64_t)INT32_MAX / mx::kGemmThreads)
     return MXFP8_ERR_OVERFLOW;
-  // The kernel runs a last round of at most half the CUs' worth of tiles as
-  // half tiles (k_mx_gemm): the grid holds those work items, in the
-  // M-grouped form an upper bound (tiles + CUs / 2).  The CU count is the
-  // current device's; it only decides the split, not any result.
+  // The kernel runs a last round of T tiles as 2 T half tiles when T is at
+  // most half the CUs, as 4 T quarter tiles when at most a quarter
+  // (k_mx_gemm): the grid holds those work items, in the M-grouped form an
+  // upper bound (tiles + the larger of 3 (CUs / 4) and CUs / 2 extra items).
+  // The CU count is the current device's; it only decides the split, not
+  // any result.
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 0;
   if (cus > 1) {
     if (mode == mx::kGemmGroupM) {
-      blocks += cus / 2;
+      blocks += std::max<int64_t>(3 * (cus / 4), cus / 2);
     } else {
       const int64_t tail = blocks % cus;
-      if (tail > 0 && tail <= cus / 2) blocks += tail;
+      if (tail > 0 && tail <= cus / 4) blocks += 3 * tail;
+      else if (tail > 0 && tail <= cus / 2) blocks += tail;
     }
   }
   if (blocks > (int64_t)INT32_MAX / mx::kGemmThreads) return MXFP8_ERR_OVERFLOW;

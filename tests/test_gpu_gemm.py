@@ -86,29 +86,39 @@ def test_gemm_random_codes(oracle_mod, M, N, K):
 
 
 def test_gemm_half_tiles_match_whole_tiles(oracle_mod):
-    """A last round of at most half the CUs' worth of 256 x 256 tiles runs as
-    256 x 128 half tiles.  4352 x 4096 (272 tiles) and 4352 x 4352 (289)
-    over the same A put different tiles in that round, so the first 4096
-    columns of the two results come from whole tiles in one launch and half
-    tiles in the other for some elements: they must agree bit for bit (each
-    element is the same sum in the same order).  The last tile row, split
-    in both, is checked against the oracle on sampled rows and columns."""
+    """A last round of T tiles runs as 2 T 256 x 128 half tiles when T is at
+    most half the CUs, as 4 T 256 x 64 quarter tiles when at most a quarter.
+    Over the same A, 4352 x 4096 (272 tiles: 16 in the last round on 256
+    CUs), 4352 x 4352 (289: 33) and 4352 x 5120 (340: 84) put different
+    tiles in that round, run whole, halved or quartered, so their common
+    columns come from different forms in different launches: they must agree
+    bit for bit (each element is the same sum in the same order).  A's first
+    4160 rows against 4096 columns (a last round of 64-row quarter tiles)
+    must equal the same rows of the first result.  The last tile row is
+    checked against the oracle on sampled rows and columns."""
     dev = _dev()
-    M, K, N1, N2 = 4352, 512, 4096, 4352
-    print(f"case: gemm half tiles {M}x{N1}/{N2}x{K}", flush=True)
+    M, K, N1, N2, N3 = 4352, 512, 4096, 4352, 5120
+    print(f"case: gemm half and quarter tiles {M}x{N1}/{N2}/{N3}x{K}", flush=True)
     rng = np.random.default_rng(77)
     a, sa = _rand_operands(rng, M, K)
-    b, sb = _rand_operands(rng, N2, K)
+    b, sb = _rand_operands(rng, N3, K)
     A, SA, B, SB = _to_dev(a, dev), _to_dev(sa, dev), _to_dev(b, dev), _to_dev(sb, dev)
     c1 = mx.mxfp8_gemm(A, SA, B[:N1], SB[:N1])
-    c2 = mx.mxfp8_gemm(A, SA, B, SB)
+    c2 = mx.mxfp8_gemm(A, SA, B[:N2], SB[:N2])
+    c3 = mx.mxfp8_gemm(A, SA, B, SB)
+    c4 = mx.mxfp8_gemm(A[:4160], SA[:4160], B[:N1], SB[:N1])
     torch.cuda.synchronize()
     assert torch.equal(c2[:, :N1], c1)
-    rows = np.unique(np.concatenate([[0, 4095, 4096, 4223, 4224, M - 1], rng.integers(4096, M, 10),
+    assert torch.equal(c3[:, :N2], c2)
+    assert torch.equal(c4, c1[:4160])
+    rows = np.unique(np.concatenate([[0, 3071, 3072, 4095, 4096, 4223, 4224, M - 1], rng.integers(3072, M, 10),
                                      rng.integers(0, M, 6)]))
-    cols = np.unique(np.concatenate([[0, 127, 128, 255, 256, N2 - 129, N2 - 128, N2 - 1], rng.integers(0, N2, 40)]))
-    got = c2.cpu().numpy()[rows][:, cols]
+    cols = np.unique(np.concatenate([[0, 63, 64, 127, 128, 255, 256, N2 - 1, N2, N3 - 65, N3 - 64, N3 - 1],
+                                     rng.integers(0, N3, 40)]))
+    got = c3.cpu().numpy()[rows][:, cols]
     _check(oracle_mod, "half_tiles", a[rows], sa[rows], b[cols], sb[cols], got)
+    cols1 = cols[cols < N1]
+    _check(oracle_mod, "quarter_tiles", a[rows], sa[rows], b[cols1], sb[cols1], c1.cpu().numpy()[rows][:, cols1])
 
 
 @pytest.mark.parametrize("tail", [1, 32, 64, 65, 128, 129])
