@@ -31,7 +31,9 @@
 // would leave at least half the CUs idle runs as 256 x 128 half tiles (at
 // least three quarters idle: 256 x 64 quarter tiles), and
 // a tile of at most 128 rows computes and loads only the row blocks that
-// can hold its rows.  Unaligned scale rows are read as 4-byte words.
+// can hold its rows.  In the M-grouped form every group's whole row tiles
+// run before the groups' partial last rows.  Unaligned scale rows are read
+// as 4-byte words.
 #pragma once
 #include "mx_kernels.hpp"
 
@@ -123,7 +125,8 @@ __device__ __forceinline__ void wait_vm() {
 // quarter; each wavefront 128 x 32 NJ), for the last partial round of
 // tiles.  Every element of C gets the same sum in the same order either
 // way.  L is the tile's index in the tile order over tiles_m rows of
-// tiles (in the grouped form the real count).
+// tiles (in the grouped form the real count, of which full_m are whole
+// rows of 256, ordered before the groups' partial last rows).
 //
 // The tile's 32-row blocks alternate between the two wavefront rows
 // (wavefront row wm takes blocks wm, wm + 2, wm + 4, wm + 6), so that a
@@ -139,7 +142,7 @@ __device__ __forceinline__ void wait_vm() {
 template <int MODE, bool NT, int NJ, int NI = 4>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlot], uint8_t (*smB)[kSlot],
                                           uint8_t (*smS)[kBM + kBN][kSG], const int32_t *offs_s, u32 L, int half,
-                                          int64_t tiles_m) {
+                                          int64_t tiles_m, int64_t full_m) {
   const u32 L_in = L;
   constexpr int BN = 64 * NJ;     // tile columns
   constexpr int WBN = 32 * NJ;    // columns per wavefront
@@ -158,10 +161,23 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
     kgrp = L / per;
     L %= per;
   }
+  // In the M-grouped form the whole row tiles of every group come first and
+  // the groups' partial last row tiles after them, each set in this order.
+  u32 rows_set = (u32)tiles_m, row0 = 0;
+  if constexpr (MODE == kGemmGroupM) {
+    const u32 n_full = (u32)full_m * (u32)g.tiles_n;
+    if (L >= n_full) {
+      L -= n_full;
+      rows_set = (u32)(tiles_m - full_m);
+      row0 = (u32)full_m;
+    } else {
+      rows_set = (u32)full_m;
+    }
+  }
   const u32 per_group = (u32)kGroup * (u32)g.tiles_n;
   const u32 grp = L / per_group, in_grp = L % per_group;
-  const u32 rows_in_grp = min((u32)kGroup, (u32)tiles_m - grp * (u32)kGroup);
-  const int64_t tm = (int64_t)grp * kGroup + in_grp % rows_in_grp;
+  const u32 rows_in_grp = min((u32)kGroup, rows_set - grp * (u32)kGroup);
+  const int64_t tm = (int64_t)row0 + (int64_t)grp * kGroup + in_grp % rows_in_grp;
   const int64_t n_base = (int64_t)(in_grp / rows_in_grp) * kBN + (int64_t)half * BN;
   if (n_base >= g.N) return;  // the second half of a tile narrower than 128 columns (uniform)
 
@@ -175,14 +191,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
   int64_t k_lo = 0, Kt = g.K, s_lo = 0;
   float *c_mat = g.c;
   if constexpr (MODE == kGemmGroupM) {
+    // row tile tm < full_m: the (tm - whole rows before)-th whole row of the
+    // group it falls in; otherwise the partial last row of the
+    // (tm - full_m)-th group that has one
     int64_t start = 0, before = 0;
     int e_hit = -1;
+    const bool whole = tm < full_m;
+    const int64_t want = whole ? tm : tm - full_m;
     for (int e = 0; e < g.G; e++) {  // uniform: every lane walks the same offsets
       const int64_t end = min<int64_t>(max<int64_t>((int64_t)offs_s[e], start), g.M);
-      const int64_t nt = (end - start + kBM - 1) / kBM;
-      if (tm < before + nt) {
+      const int64_t nf = (end - start) / kBM;
+      const int64_t nt = whole ? nf : (int64_t)((end - start) % kBM != 0);
+      if (want < before + nt) {
         e_hit = e;
-        m_base = start + (tm - before) * kBM;
+        m_base = start + (whole ? want - before : nf) * kBM;
         m_end = end;
         break;
       }
@@ -223,11 +245,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, uint8_t (*smA)[kSlo
   const u32 a_rows = (u32)min<int64_t>(m_end - m_base, kBM), b_rows = (u32)min<int64_t>(g.N - n_base, BN);
   if constexpr (NI == 4) {
     if (a_rows <= 2u * 32u) {  // uniform: a short tile, one row block per wavefront
-      gemm_tile<MODE, NT, NJ, 1>(g, smA, smB, smS, offs_s, L_in, half, tiles_m);
+      gemm_tile<MODE, NT, NJ, 1>(g, smA, smB, smS, offs_s, L_in, half, tiles_m, full_m);
       return;
     }
     if (a_rows <= 4u * 32u) {  // two row blocks per wavefront
-      gemm_tile<MODE, NT, NJ, 2>(g, smA, smB, smS, offs_s, L_in, half, tiles_m);
+      gemm_tile<MODE, NT, NJ, 2>(g, smA, smB, smS, offs_s, L_in, half, tiles_m, full_m);
       return;
     }
   }
@@ -586,19 +608,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t smS[2][kBM + kBN][kSG];
   __shared__ int32_t offs_s[MODE == kGemmGroupM ? kMaxGroups : 1];
 
-  int64_t tiles_m = g.tiles_m;
+  int64_t tiles_m = g.tiles_m, full_m = g.tiles_m;
   if constexpr (MODE == kGemmGroupM) {
     for (int e = threadIdx.x; e < g.G; e += kGemmThreads) offs_s[e] = g.offs[e];
     __syncthreads();
     // real tile rows: every group's rows rounded up to whole tiles, with the
-    // offsets clamped into ordered groups within [0, M] as the tiles see them
-    int64_t start = 0, n = 0;
+    // offsets clamped into ordered groups within [0, M] as the tiles see
+    // them; full_m of them hold 256 rows
+    int64_t start = 0, n = 0, nf = 0;
     for (int e = 0; e < g.G; e++) {  // uniform
       const int64_t end = min<int64_t>(max<int64_t>((int64_t)offs_s[e], start), g.M);
       n += (end - start + kBM - 1) / kBM;
+      nf += (end - start) / kBM;
       start = end;
     }
     tiles_m = n;
+    full_m = nf;
   }
   const u32 R = (u32)(MODE == kGemmGroupK ? (int64_t)g.G : 1) * (u32)tiles_m * (u32)g.tiles_n;
   const u32 C = g.cus > 1 ? (u32)g.cus : 1u;
@@ -621,13 +646,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mx_gemm(const GemmArgs g) {
         L = (p / share) * per + x * share + p % share;
       }
     }
-    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, L, 0, tiles_m);
+    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, L, 0, tiles_m, full_m);
   } else if (parts == 1) {
-    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, b, 0, tiles_m);
+    gemm_tile<MODE, NT, 4>(g, smA, smB, smS, offs_s, b, 0, tiles_m, full_m);
   } else if (parts == 2) {
-    gemm_tile<MODE, NT, 2>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 2, (int)((b - R0) & 1u), tiles_m);
+    gemm_tile<MODE, NT, 2>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 2, (int)((b - R0) & 1u), tiles_m, full_m);
   } else {
-    gemm_tile<MODE, NT, 1>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 4, (int)((b - R0) & 3u), tiles_m);
+    gemm_tile<MODE, NT, 1>(g, smA, smB, smS, offs_s, R0 + (b - R0) / 4, (int)((b - R0) & 3u), tiles_m, full_m);
   }
 }
 
