@@ -416,6 +416,39 @@ def test_grouped_gemm_one_group_is_the_plain_gemm():
     assert torch.equal(plain, grouped)
 
 
+def test_grouped_gemm_partial_rows_in_full_rounds(oracle_mod):
+    """The M-grouped form runs every group's whole 256-row tiles before the
+    groups' partial last rows.  Five groups over 4500 rows (1000 rows each,
+    then 500) against 4096 columns: 13 whole tile rows and 5 partial ones,
+    288 tiles, so on 256 CUs partial tiles run both in the full round and in
+    a last round of quarter tiles.  Every group's rows must equal, bit for
+    bit, the plain GEMM of those rows with that group's expert, and sampled
+    rows (most in partial tiles) match the oracle."""
+    dev = _dev()
+    M, N, K, G = 4500, 4096, 256, 5
+    ends = [1000, 2000, 3000, 4000, 4500]
+    print(f"case: grouped gemm partial rows in full rounds {M}x{N}x{K} G={G}", flush=True)
+    rng = np.random.default_rng(31)
+    a, sa = _rand_operands(rng, M, K)
+    b, sb = _rand_operands(rng, G * N, K)
+    A, SA = _to_dev(a, dev), _to_dev(sa, dev)
+    B, SB = _to_dev(b, dev).view(G, N, K), _to_dev(sb, dev).view(G, N, K // 32)
+    got = mx.mxfp8_grouped_gemm(A, SA, B, SB, torch.tensor(ends, dtype=torch.int32, device=dev))
+    start = 0
+    for g, end in enumerate(ends):
+        plain = mx.mxfp8_gemm(A[start:end], SA[start:end], B[g], SB[g])
+        torch.cuda.synchronize()
+        assert torch.equal(got[start:end], plain), f"group {g}"
+        start = end
+    rows = np.array([768, 999, 1768, 3999, 4000, 4255, 4256, 4499])  # partial rows; 4000 and 4255 in a whole tile
+    cols = np.unique(np.concatenate([[0, 63, 64, N - 1], rng.integers(0, N, 12)]))
+    host = got.cpu().numpy()
+    for r in rows:
+        g = int(np.searchsorted(ends, r, side="right"))
+        bg, sbg = b[g * N:(g + 1) * N], sb[g * N:(g + 1) * N]
+        _check(oracle_mod, f"grouped_partial_row{r}", a[[r]], sa[[r]], bg[cols], sbg[cols], host[[r]][:, cols])
+
+
 def test_grouped_gemm_16640x8192x5120_g4_sampled(oracle_mod):
     """The pages' grouped shape (16640 tokens, 4 experts of 8192 x 5120),
     operands from the casts, uneven groups; sampled rows of every group."""
