@@ -98,11 +98,17 @@ def bench_calls(workload: str, experts: int):
                                        ("wgrad_grouped_gemm_k_8192x5120_t16640_g4", 2, 8192, 5120, 16640, 4)):
         tiles_m = -(-gm // 256) + (G if mode == 1 else 0)
         grid = tiles_m * -(-gn // 256) * (G if mode == 2 else 1)
-        # the launch grid as mxfp8.hip sizes it: a short last round of tiles
-        # runs as half tiles (room for CUS / 2 of them in the grouped form,
-        # whose tile count the host does not know)
+        # the launch grid as mxfp8.hip sizes it: a short last round of T
+        # tiles runs as 2 T half tiles (T <= CUS / 2) or 4 T quarter tiles
+        # (T <= CUS / 4); the grouped form, whose tile count the host does
+        # not know, has room for the larger of 3 (CUS / 4) and CUS / 2 extra
         tail = grid % CUS
-        grid += CUS // 2 if mode == 1 else (tail if 0 < tail <= CUS // 2 else 0)
+        if mode == 1:
+            grid += max(3 * (CUS // 4), CUS // 2)
+        elif 0 < tail <= CUS // 4:
+            grid += 3 * tail
+        elif 0 < tail <= CUS // 2:
+            grid += tail
         rd = gm * gk + gn * gk * (G if mode == 1 else 1)
         calls.append(Call(f"k_mx_gemm<{mode},", label, rd, 4 * gm * gn * (G if mode == 2 else 1), grid,
                           2 * gm * gn * gk))
