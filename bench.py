@@ -571,10 +571,11 @@ def run_detail(inp, fwd_out, bwd_out, stream, core_only=False):
     cg = torch.empty((gm, gn), dtype=torch.float32, device=inp.gate.device)
     # 10 warm-up launches: after the pause for its inputs the GPU's clocks
     # take a few launches of this compute-bound kernel to come back up
-    avg, _ = time_launches(lambda: mx.mxfp8_gemm(qa, sa, qb, sb, out=cg, stream=stream), 20, 10)
+    avg, med = time_launches(lambda: mx.mxfp8_gemm(qa, sa, qb, sb, out=cg, stream=stream), 20, 10)
     tflops = 2.0 * gm * gn * gk / avg / 1e12
     res["gemm_16384x8192x5120"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
-                                   "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+                                   "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4),
+                                   "median_us": round(med * 1e6, 2)}
     del qa, qb, sa, sb, cg
     torch.cuda.empty_cache()
     # grouped form at the pages' shape: 16640 tokens over 4 experts of 8192 x
@@ -588,10 +589,11 @@ def run_detail(inp, fwd_out, bwd_out, stream, core_only=False):
     offs = torch.arange(1, ng + 1, dtype=torch.int32, device=inp.gate.device) * (gm // ng)
     cg = torch.empty((gm, gn), dtype=torch.float32, device=inp.gate.device)
     qb3, sb3 = qb.view(ng, gn, gk), sb.view(ng, gn, gk // 32)
-    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm(qa, sa, qb3, sb3, offs, out=cg, stream=stream), 20, 10)
+    avg, med = time_launches(lambda: mx.mxfp8_grouped_gemm(qa, sa, qb3, sb3, offs, out=cg, stream=stream), 20, 10)
     tflops = 2.0 * gm * gn * gk / avg / 1e12
     res["grouped_gemm_16640x8192x5120_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
-                                              "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+                                              "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4),
+                                              "median_us": round(med * 1e6, 2)}
     del qa, qb, sa, sb, qb3, sb3, cg
     torch.cuda.empty_cache()
     # the input gradient at the same shape, its expert operand the 3D cast's
@@ -602,10 +604,11 @@ def run_detail(inp, fwd_out, bwd_out, stream, core_only=False):
     q3, s3 = mx.mxfp8_quant_3d_colwise(w3, stream=stream)
     del w3
     cg = torch.empty((gm, gk), dtype=torch.float32, device=inp.gate.device)
-    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm(qa, sa, q3, s3, offs, out=cg, stream=stream), 20, 10)
+    avg, med = time_launches(lambda: mx.mxfp8_grouped_gemm(qa, sa, q3, s3, offs, out=cg, stream=stream), 20, 10)
     tflops = 2.0 * gm * gn * gk / avg / 1e12
     res["dgrad_grouped_gemm_16640x5120x8192_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
-                                                    "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+                                                    "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4),
+                                                    "median_us": round(med * 1e6, 2)}
     del qa, sa, q3, s3, cg
     # the weight gradient: dW_g [8192, 5120] = dy_g^T x_g over each expert's
     # tokens, operands the grouped colwise casts (per-group padded scales)
@@ -618,10 +621,11 @@ def run_detail(inp, fwd_out, bwd_out, stream, core_only=False):
     _, qb, _, sb = mx.mxfp8_quant_2d_grouped(x, ends, stream=stream)
     del dy, x
     cw = torch.empty((ng, gn, gk), dtype=torch.float32, device=inp.gate.device)
-    avg, _ = time_launches(lambda: mx.mxfp8_grouped_gemm_k(qa, sa, qb, sb, ends, out=cw, stream=stream), 20, 10)
+    avg, med = time_launches(lambda: mx.mxfp8_grouped_gemm_k(qa, sa, qb, sb, ends, out=cw, stream=stream), 20, 10)
     tflops = 2.0 * gm * gn * gk / avg / 1e12
     res["wgrad_grouped_gemm_k_8192x5120_t16640_g4"] = {"us": round(avg * 1e6, 2), "TFLOP/s": round(tflops, 1),
-                                                       "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4)}
+                                                       "frac": round(tflops / metrics.MFMA_FP8_PEAK_TFLOPS, 4),
+                                                       "median_us": round(med * 1e6, 2)}
     del qa, sa, qb, sb, cw, offs, ends
     torch.cuda.empty_cache()
     # the grouped casts at 131072 x 8192 (8 token groups): colwise scales in
